@@ -1,0 +1,207 @@
+// C-ABI entry points of libsxattn (declared in include/sxattn.h): host-side
+// argument validation, kernel selection and launch on the caller's stream.
+// Every status other than SXA_OK leaves a message in a thread-local buffer that
+// sxa_last_error() returns.  No C++ exception crosses the ABI.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+namespace sxa {
+int lpt_assign_host(const int64_t* cost, int32_t n_chunk, int32_t n_bin, int32_t* bin_of_chunk,
+                    int64_t* bin_load);
+}
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SXA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SXA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(sxa_dtype t) { return t == SXA_F32 || t == SXA_BF16; }
+
+// Shared validation of the attention arguments; fills `a` on success.
+int check_attn(const void* q, const void* k, const void* v, sxa_dtype in_dtype, int32_t n_blk,
+               int32_t block_size, int32_t hq, int32_t hkv, int32_t d, float scale,
+               const int32_t* anchor, const int32_t* sample_start, const int32_t* chunk_gstart,
+               const int32_t* chunk_len, int32_t n_chunk, int64_t n_loc, const void* k_self,
+               const void* v_self, sxa::AttnArgs& a) {
+  if (!dtype_ok(in_dtype)) return fail(SXA_EINVAL, "in_dtype %d is not a valid sxa_dtype", in_dtype);
+  if (block_size != sxa::kBlock)
+    return fail(SXA_EUNSUPPORTED, "block_size %d is not supported (only 16)", block_size);
+  if (d != 64 && d != 128) return fail(SXA_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", d);
+  if (n_blk < 0) return fail(SXA_EINVAL, "n_blk must be >= 0 (got %d)", n_blk);
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+    return fail(SXA_EINVAL, "hq (%d) must be a positive multiple of hkv (%d)", hq, hkv);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(SXA_EINVAL, "scale must be positive and finite (got %g)", static_cast<double>(scale));
+  if (n_chunk < 0) return fail(SXA_EINVAL, "n_chunk must be >= 0 (got %d)", n_chunk);
+  if (n_loc < 0) return fail(SXA_EINVAL, "n_loc must be >= 0");
+  if (n_chunk == 0 && n_loc != 0) return fail(SXA_EINVAL, "n_loc must be 0 when n_chunk is 0");
+  if (static_cast<int64_t>(n_blk) * sxa::kBlock * hq * d >= (int64_t{1} << 40))
+    return fail(SXA_EINVAL, "query tensor too large");
+  if ((k_self == nullptr) != (v_self == nullptr))
+    return fail(SXA_EINVAL, "k_self and v_self must be both NULL or both non-NULL");
+  if (n_blk > 0 && (q == nullptr || anchor == nullptr || sample_start == nullptr))
+    return fail(SXA_EINVAL, "q, anchor and sample_start must not be NULL");
+  if (n_chunk > 0 && (chunk_gstart == nullptr || chunk_len == nullptr))
+    return fail(SXA_EINVAL, "chunk_gstart and chunk_len must not be NULL when n_chunk > 0");
+  if (n_loc > 0 && (k == nullptr || v == nullptr)) return fail(SXA_EINVAL, "k and v must not be NULL");
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_self = k_self;
+  a.v_self = v_self;
+  a.n_blk = n_blk;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.scale = scale;
+  a.anchor = anchor;
+  a.sample_start = sample_start;
+  a.chunk_gstart = chunk_gstart;
+  a.chunk_len = chunk_len;
+  a.n_chunk = n_chunk;
+  a.n_loc = n_loc;
+  return SXA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sxa_last_error(void) { return g_err; }
+
+int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_dtype,
+                     int32_t n_blk, int32_t block_size, int32_t hq, int32_t hkv, int32_t d,
+                     float scale, const int32_t* anchor, const int32_t* sample_start,
+                     const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
+                     int64_t n_loc, const void* k_self, const void* v_self, void* o,
+                     sxa_dtype o_dtype, float* lse, void* stream) {
+  sxa::AttnArgs a;
+  int st = check_attn(q, k, v, in_dtype, n_blk, block_size, hq, hkv, d, scale, anchor,
+                      sample_start, chunk_gstart, chunk_len, n_chunk, n_loc, k_self, v_self, a);
+  if (st != SXA_OK) return st;
+  if (!dtype_ok(o_dtype)) return fail(SXA_EINVAL, "o_dtype %d is not a valid sxa_dtype", o_dtype);
+  if (in_dtype == SXA_F32 && o_dtype != SXA_F32)
+    return fail(SXA_EUNSUPPORTED, "float32 inputs need a float32 output");
+  if (n_blk > 0 && (o == nullptr || lse == nullptr)) return fail(SXA_EINVAL, "o and lse must not be NULL");
+  a.o = o;
+  a.o_bf16 = o_dtype == SXA_BF16;
+  a.lse = lse;
+  if (n_blk == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(in_dtype == SXA_BF16 ? sxa::launch_fwd_bf16(a, s) : sxa::launch_fwd_f32(a, s),
+                    "sparse_xattn_fwd launch");
+}
+
+int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_dtype,
+                     int32_t n_blk, int32_t block_size, int32_t hq, int32_t hkv, int32_t d,
+                     float scale, const int32_t* anchor, const int32_t* sample_start,
+                     const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
+                     int64_t n_loc, const void* k_self, const void* v_self, const void* o,
+                     const void* dout, const float* lse, float* delta_ws, float* dq_accum,
+                     void* dk, void* dv, void* dk_self, void* dv_self, void* stream) {
+  sxa::AttnArgs a;
+  int st = check_attn(q, k, v, in_dtype, n_blk, block_size, hq, hkv, d, scale, anchor,
+                      sample_start, chunk_gstart, chunk_len, n_chunk, n_loc, k_self, v_self, a);
+  if (st != SXA_OK) return st;
+  if (n_blk > 0 && (o == nullptr || dout == nullptr || lse == nullptr || delta_ws == nullptr ||
+                    dq_accum == nullptr))
+    return fail(SXA_EINVAL, "o, dout, lse, delta_ws and dq_accum must not be NULL");
+  if (n_loc > 0 && (dk == nullptr || dv == nullptr)) return fail(SXA_EINVAL, "dk and dv must not be NULL");
+  if (k_self != nullptr && (dk_self == nullptr || dv_self == nullptr))
+    return fail(SXA_EINVAL, "dk_self and dv_self must not be NULL when k_self is given");
+  a.o_in = o;
+  a.dout = dout;
+  a.lse_in = lse;
+  a.delta = delta_ws;
+  a.dq = dq_accum;
+  a.dk = dk;
+  a.dv = dv;
+  a.dk_self = dk_self;
+  a.dv_self = dv_self;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_blk == 0) {
+    // no query: the gradients of the local keys/values are zero
+    const int64_t es = in_dtype == SXA_BF16 ? 2 : 4;
+    const int64_t kv_words = n_loc * hkv * d * es / 4;
+    hipError_t e = sxa::launch_zero_words(dk, kv_words, s);
+    if (e == hipSuccess) e = sxa::launch_zero_words(dv, kv_words, s);
+    return hip_status(e, "sparse_xattn_bwd zero fill");
+  }
+  return hip_status(in_dtype == SXA_BF16 ? sxa::launch_bwd_bf16(a, s) : sxa::launch_bwd_f32(a, s),
+                    "sparse_xattn_bwd launch");
+}
+
+int lse_combine(const void* o_parts, sxa_dtype part_dtype, const float* lse_parts,
+                int32_t n_parts, int64_t rows, int32_t d, void* o_out, sxa_dtype out_dtype,
+                float* lse_out, void* stream) {
+  if (!dtype_ok(part_dtype) || !dtype_ok(out_dtype)) return fail(SXA_EINVAL, "invalid dtype");
+  if (n_parts < 0 || rows < 0) return fail(SXA_EINVAL, "n_parts and rows must be >= 0");
+  if (d != 64 && d != 128 && d != 256) return fail(SXA_EUNSUPPORTED, "d %d is not supported (64, 128, 256)", d);
+  if (rows > 0 && (o_out == nullptr || lse_out == nullptr)) return fail(SXA_EINVAL, "outputs must not be NULL");
+  if (rows > 0 && n_parts > 0 && (o_parts == nullptr || lse_parts == nullptr))
+    return fail(SXA_EINVAL, "inputs must not be NULL");
+  if (rows >= (int64_t{1} << 34)) return fail(SXA_EINVAL, "rows too large");
+  if (rows == 0) return ok();
+  return hip_status(sxa::launch_combine(o_parts, part_dtype == SXA_BF16, lse_parts, n_parts, rows, d,
+                                        o_out, out_dtype == SXA_BF16, lse_out,
+                                        static_cast<hipStream_t>(stream)),
+                    "lse_combine launch");
+}
+
+int chunk_cost(const int32_t* anchor, const int32_t* sample_start, int32_t n_blk,
+               int32_t block_size, int32_t n_ctx, int32_t chunk_size, int64_t* cost_out,
+               void* stream) {
+  if (block_size != sxa::kBlock)
+    return fail(SXA_EUNSUPPORTED, "block_size %d is not supported (only 16)", block_size);
+  if (n_blk < 0 || n_ctx < 0) return fail(SXA_EINVAL, "n_blk and n_ctx must be >= 0");
+  if (chunk_size <= 0) return fail(SXA_EINVAL, "chunk_size must be > 0 (got %d)", chunk_size);
+  if (n_ctx > 0 && cost_out == nullptr) return fail(SXA_EINVAL, "cost_out must not be NULL");
+  if (n_blk > 0 && (anchor == nullptr || sample_start == nullptr))
+    return fail(SXA_EINVAL, "anchor and sample_start must not be NULL");
+  const int64_t n_chunk = (static_cast<int64_t>(n_ctx) + chunk_size - 1) / chunk_size;
+  if (n_chunk == 0) return ok();
+  if (n_blk == 0) {
+    return hip_status(sxa::launch_zero_words(cost_out, 2 * n_chunk, static_cast<hipStream_t>(stream)),
+                      "chunk_cost zero fill");
+  }
+  return hip_status(sxa::launch_chunk_cost(anchor, sample_start, n_blk, n_ctx, chunk_size, cost_out,
+                                           static_cast<hipStream_t>(stream)),
+                    "chunk_cost launch");
+}
+
+int lpt_assign(const int64_t* cost, int32_t n_chunk, int32_t n_bin, int32_t* bin_of_chunk,
+               int64_t* bin_load) {
+  if (n_bin <= 0) return fail(SXA_EINVAL, "n_bin must be > 0 (got %d)", n_bin);
+  if (n_chunk <= 0 || n_chunk % n_bin != 0)
+    return fail(SXA_EINVAL, "n_chunk (%d) must be a positive multiple of n_bin (%d)", n_chunk, n_bin);
+  if (cost == nullptr || bin_of_chunk == nullptr || bin_load == nullptr)
+    return fail(SXA_EINVAL, "cost, bin_of_chunk and bin_load must not be NULL");
+  for (int32_t i = 0; i < n_chunk; ++i)
+    if (cost[i] < 0) return fail(SXA_EINVAL, "cost[%d] is negative", i);
+  sxa::lpt_assign_host(cost, n_chunk, n_bin, bin_of_chunk, bin_load);
+  return ok();
+}
+
+}  // extern "C"

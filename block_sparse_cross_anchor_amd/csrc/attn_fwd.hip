@@ -1,0 +1,421 @@
+// bf16 forward of the anchor-masked block-sparse cross-attention on gfx950 MFMA.
+//
+// What is computed ("Split-KV speeds diffusion drafter training...", sections
+// "Why short queries change the problem" and "Exchange the smaller side"): for
+// every query row (token i of block b, head h) the softmax over the allowed keys
+// of this call -- context positions [sample_start[b], anchor[b]) inside the local
+// chunks, plus the 16 own-block keys when k_self is given -- giving the partial
+// output O and its natural-log log-sum-exp, from which partials merge exactly.
+//
+// Work decomposition
+//   * Rows of one kv head g: r = token * grp + (h - g*grp), grp = hq / hkv.  With
+//     grp = 4 the 64 rows of one wave are one block's 16 tokens x 4 heads, which
+//     share one mask.  A workgroup (4 waves) owns 256 consecutive rows of one kv
+//     head: for grp = 4 that is 4 consecutive blocks, normally of one sample, so
+//     their key intervals start at the same position and K/V tiles are shared
+//     through LDS.
+//   * Linear workgroup id L -> (kv head L % hkv, row group L / hkv): consecutive
+//     ids are dispatched round-robin over the 8 XCDs, so with hkv = 8 each XCD
+//     serves one kv head and its K/V stays in that XCD's L2.
+//   * Keys are visited in tiles of 64 rows: first the own-block rows of the
+//     workgroup's blocks, then, chunk by chunk, the tiles (aligned to the chunk
+//     start) that meet the union of the workgroup's intervals.  Each wave skips
+//     the MFMAs of tiles outside all of its rows' intervals (anchor-driven tile
+//     skipping) and masks only tiles that are partially allowed.
+//
+// MFMA formulation (v_mfma_f32_32x32x16_bf16; lane l, half h = l / 32):
+//   S^T = K Q^T   A = K tile rows (from LDS), B = Q^T (registers, whole kernel)
+//                 result lane l holds column (query row) l % 32 and keys
+//                 8*(r/4) + 4h + r%4 of the 32-key M tile.
+//   O^T += V^T P^T with P^T taken straight from the S^T registers (converted to
+//                 bf16); the A operand is V^T, stored transposed in LDS with the
+//                 keys of each 16-key step permuted (bits 2 and 3 swapped) so that
+//                 the 8 keys a lane needs are one 16-byte read.
+//   Row max needs one exchange between the two lane halves; row sums are kept
+//   per half and added once at the end.
+//   Both LDS tiles are XOR-swizzled in 16-byte units so that the 8-lane groups of
+//   ds_read_b128 hit distinct banks.
+// Online softmax in base 2: x = s * scale * log2(e); p = exp2(x - m).
+#include "device_common.h"
+#include "internal.h"
+
+namespace sxa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerWG = 256;
+constexpr int kTileKeys = 64;
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* k_self;
+  const uint16_t* v_self;
+  const int32_t* anchor;
+  const int32_t* sample_start;
+  const int32_t* chunk_gstart;
+  const int32_t* chunk_len;
+  void* o;
+  float* lse;
+  int32_t n_blk, hq, hkv, n_chunk;
+  float scale_log2;  // scale * log2(e)
+};
+
+struct Tile {
+  int64_t row0;  // first source row (local K/V row, or own-block row)
+  int nrows;     // valid rows (<= 64)
+  int coord0;    // key coordinate of row0: global position, or own-block row index
+  int self;      // 1: own-block tile
+};
+
+// Sequence of key tiles of one workgroup (uniform across the workgroup).
+struct Walk {
+  int self_pos, self_end;
+  int c;
+  int64_t off;
+  int gs, len, t, t_end;
+};
+
+__device__ __forceinline__ bool walk_next(Walk& w, const int32_t* __restrict__ cgs,
+                                          const int32_t* __restrict__ clen, int n_chunk, int LO,
+                                          int HI, Tile& out) {
+  if (w.self_pos < w.self_end) {
+    out.row0 = w.self_pos;
+    out.nrows = min(kTileKeys, w.self_end - w.self_pos);
+    out.coord0 = w.self_pos;
+    out.self = 1;
+    w.self_pos += kTileKeys;
+    return true;
+  }
+  while (true) {
+    if (w.t < w.t_end) {
+      out.row0 = w.off + static_cast<int64_t>(w.t) * kTileKeys;
+      out.nrows = min(kTileKeys, w.len - w.t * kTileKeys);
+      out.coord0 = w.gs + w.t * kTileKeys;
+      out.self = 0;
+      ++w.t;
+      return true;
+    }
+    if (w.c >= n_chunk) return false;
+    w.off += w.len;
+    ++w.c;
+    if (w.c >= n_chunk) {
+      w.len = 0;
+      return false;
+    }
+    w.gs = cgs[w.c];
+    w.len = clen[w.c];
+    const int a = max(LO, w.gs), e = min(HI, w.gs + w.len);
+    if (a < e) {
+      w.t = (a - w.gs) / kTileKeys;
+      w.t_end = (e - w.gs + kTileKeys - 1) / kTileKeys;
+    } else {
+      w.t = w.t_end = 0;
+    }
+  }
+}
+
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// key position inside a 64-key V^T row: bits 2 and 3 of the key index swapped
+__device__ __forceinline__ int vt_pos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+__device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
+
+template <int D>
+struct TileRegs {
+  static constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  static constexpr int KLOADS = kTileKeys * CPR / kThreads;  // K chunks per thread
+  static constexpr int VITEMS = kTileKeys / 4 * CPR;         // (key quad, chunk) items
+  u32x4 k[KLOADS];
+  u32x4 v[4];
+
+  __device__ __forceinline__ void load(const Tile& t, const FwdParams& p, int g, int tid) {
+    const uint16_t* K = t.self ? p.k_self : p.k;
+    const uint16_t* V = t.self ? p.v_self : p.v;
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int idx = tid + kThreads * i;
+      const int key = idx / CPR, j = idx % CPR;
+      if (key < t.nrows)
+        k[i] = *reinterpret_cast<const u32x4*>(K + ((t.row0 + key) * p.hkv + g) * D + 8 * j);
+      else
+        k[i] = u32x4{0, 0, 0, 0};
+    }
+    if (tid < VITEMS) {
+      const int q4 = tid / CPR, j = tid % CPR;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int key = 4 * q4 + kk;
+        if (key < t.nrows)
+          v[kk] = *reinterpret_cast<const u32x4*>(V + ((t.row0 + key) * p.hkv + g) * D + 8 * j);
+        else
+          v[kk] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* lk, uint16_t* lv, int tid) const {
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int idx = tid + kThreads * i;
+      const int key = idx / CPR, j = idx % CPR;
+      *reinterpret_cast<u32x4*>(lk + key * D + 8 * (j ^ (key & 7))) = k[i];
+    }
+    if (tid < VITEMS) {
+      const int q4 = tid / CPR, j = tid % CPR;
+      const int pos = vt_pos(4 * q4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * j + e;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(v[1][e >> 1], v[0][e >> 1], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(v[3][e >> 1], v[2][e >> 1], sel);
+        const int phys = ((pos >> 3) ^ vt_swz(d));
+        *reinterpret_cast<u32x2*>(lv + d * kTileKeys + 8 * phys + (pos & 7)) = u32x2{lo, hi};
+      }
+    }
+  }
+};
+
+template <int D, bool OUT_BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(1, 1))) void
+fwd_bf16_kernel(FwdParams p) {
+  constexpr int KS = D / 16;  // k-steps of S^T
+  constexpr int DT = D / 32;  // 32-row d tiles of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileKeys * D];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
+  const int g = blockIdx.x % p.hkv;
+  const int wg = blockIdx.x / p.hkv;
+  const int grp = p.hq / p.hkv;
+  const int64_t R = static_cast<int64_t>(p.n_blk) * kBlock * grp;
+  const int64_t wg_row0 = static_cast<int64_t>(wg) * kRowsPerWG;
+  const int64_t wg_last = min(wg_row0 + kRowsPerWG - 1, R - 1);
+  const int b_first = static_cast<int>(wg_row0 / grp / kBlock);
+  const int b_last = static_cast<int>(wg_last / grp / kBlock);
+  int LO = 0x7fffffff, HI = -0x7fffffff;
+  for (int b = b_first; b <= b_last; ++b) {
+    LO = min(LO, p.sample_start[b]);
+    HI = max(HI, p.anchor[b]);
+  }
+
+  // per-lane query columns (one per 32-row N tile)
+  int clo[2], chi[2], slo[2], shi[2];
+  int64_t orow[2];
+  bool valid[2];
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t r = wg_row0 + 64 * wave + 32 * nt + l32;
+    valid[nt] = r < R;
+    const int64_t rr = valid[nt] ? r : 0;
+    const int64_t tok = rr / grp;
+    const int hh = static_cast<int>(rr % grp);
+    const int blk = static_cast<int>(tok / kBlock);
+    clo[nt] = valid[nt] ? p.sample_start[blk] : 0;
+    chi[nt] = valid[nt] ? p.anchor[blk] : 0;
+    slo[nt] = valid[nt] ? kBlock * blk : 0;
+    shi[nt] = valid[nt] ? kBlock * blk + kBlock : 0;
+    orow[nt] = tok * p.hq + static_cast<int64_t>(g) * grp + hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 raw = u32x4{0, 0, 0, 0};
+      if (valid[nt]) raw = *reinterpret_cast<const u32x4*>(p.q + orow[nt] * D + 16 * ks + 8 * h2);
+      qf[nt][ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  Walk w;
+  w.self_pos = p.k_self ? kBlock * b_first : 0;
+  w.self_end = p.k_self ? kBlock * (b_last + 1) : 0;
+  w.c = -1;
+  w.off = 0;
+  w.gs = w.len = w.t = w.t_end = 0;
+
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  f32x16 oacc[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][nt][r] = 0.f;
+
+  Tile cur, nxt;
+  TileRegs<D> regs;
+  bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
+  if (have) {
+    regs.load(cur, p, g, tid);
+    regs.store(lds[0][0], lds[0][1], tid);
+    __syncthreads();
+  }
+  int buf = 0;
+  while (have) {
+    const bool has_next = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, nxt);
+    if (has_next) regs.load(nxt, p, g, tid);
+
+    // ---- this wave's share of the tile
+    int a_lo[2], a_hi[2];
+    bool any = false, full = true;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int lo = cur.self ? slo[nt] : clo[nt];
+      const int hi = cur.self ? shi[nt] : chi[nt];
+      a_lo[nt] = max(lo - cur.coord0, 0);
+      a_hi[nt] = min(hi - cur.coord0, cur.nrows);
+      any |= a_lo[nt] < a_hi[nt];
+      full &= (a_lo[nt] == 0) & (a_hi[nt] == kTileKeys);
+    }
+    if (__any(any)) {
+      const bool all_full = __all(full);
+      const uint16_t* lk = lds[buf][0];
+      const uint16_t* lv = lds[buf][1];
+      f32x16 sacc[2][2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[mt][nt][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int key = 32 * mt + l32;
+          const bf16x8 kf = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(lk + key * D + 8 * ((2 * ks + h2) ^ (key & 7))));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], sacc[mt][nt], 0, 0, 0);
+        }
+      }
+      bf16x8 pf[2][4];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if (!all_full) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = 32 * mt + 8 * (r / 4) + 4 * h2 + (r % 4);
+              if (key < a_lo[nt] || key >= a_hi[nt]) sacc[mt][nt][r] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float mnew = fmaxf(m[nt], mx * p.scale_log2);
+        const float muse = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = exp2f(m[nt] - muse);
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = exp2f(fmaf(sacc[mt][nt][r], p.scale_log2, -muse));
+            sacc[mt][nt][r] = e;
+            rs += e;
+          }
+        l[nt] = fmaf(l[nt], alpha, rs);
+        m[nt] = mnew;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            pf[nt][kq][i] = static_cast<__bf16>(sacc[kq / 2][nt][8 * (kq % 2) + i]);
+      }
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = 32 * dt + l32;
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(lv + d * kTileKeys + 8 * ((2 * kq + h2) ^ vt_swz(d))));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nt][kq], oacc[dt][nt], 0, 0, 0);
+        }
+      }
+    }
+
+    if (has_next) regs.store(lds[buf ^ 1][0], lds[buf ^ 1][1], tid);
+    __syncthreads();
+    if (!has_next) break;
+    cur = nxt;
+    buf ^= 1;
+  }
+
+  // ---- epilogue: normalise, write O and lse
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const float lt = l[nt] + swap_halves(l[nt]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (!valid[nt]) continue;
+    if (h2 == 0) p.lse[orow[nt]] = lt > 0.f ? (m[nt] + __log2f(lt)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = 32 * dt + 8 * jj + 4 * h2;
+        const float x0 = oacc[dt][nt][4 * jj] * inv, x1 = oacc[dt][nt][4 * jj + 1] * inv;
+        const float x2 = oacc[dt][nt][4 * jj + 2] * inv, x3 = oacc[dt][nt][4 * jj + 3] * inv;
+        if constexpr (OUT_BF16) {
+          uint16_t* O = static_cast<uint16_t*>(p.o) + orow[nt] * D + d0;
+          *reinterpret_cast<u32x2*>(O) =
+              u32x2{static_cast<uint32_t>(f32_to_bf16_bits(x0)) | (static_cast<uint32_t>(f32_to_bf16_bits(x1)) << 16),
+                    static_cast<uint32_t>(f32_to_bf16_bits(x2)) | (static_cast<uint32_t>(f32_to_bf16_bits(x3)) << 16)};
+        } else {
+          float* O = static_cast<float*>(p.o) + orow[nt] * D + d0;
+          *reinterpret_cast<f32x4*>(O) = f32x4{x0, x1, x2, x3};
+        }
+      }
+  }
+}
+
+template <int D, bool OUT_BF16>
+hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
+  FwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.k_self = static_cast<const uint16_t*>(a.k_self);
+  p.v_self = static_cast<const uint16_t*>(a.v_self);
+  p.anchor = a.anchor;
+  p.sample_start = a.sample_start;
+  p.chunk_gstart = a.chunk_gstart;
+  p.chunk_len = a.chunk_len;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.n_blk = a.n_blk;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.n_chunk = a.n_chunk;
+  p.scale_log2 = a.scale * kLog2e;
+  const int64_t rows = static_cast<int64_t>(a.n_blk) * kBlock * (a.hq / a.hkv);
+  const int64_t groups = (rows + kRowsPerWG - 1) / kRowsPerWG;
+  const int64_t n_wg = groups * a.hkv;
+  if (n_wg == 0) return hipSuccess;
+  fwd_bf16_kernel<D, OUT_BF16><<<dim3(static_cast<unsigned>(n_wg)), dim3(kThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.d == 64) return a.o_bf16 ? launch_d<64, true>(a, s) : launch_d<64, false>(a, s);
+  return a.o_bf16 ? launch_d<128, true>(a, s) : launch_d<128, false>(a, s);
+}
+
+}  // namespace sxa

@@ -1,0 +1,58 @@
+// Internal interface between the C-ABI host layer (api.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sxattn.h"
+
+namespace sxa {
+
+constexpr int kBlock = 16;  // draft tokens per anchor block
+
+// Everything an attention launch needs; pointers are device pointers.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* k_self;  // nullable
+  const void* v_self;
+  int32_t n_blk, hq, hkv, d;
+  float scale;
+  const int32_t* anchor;
+  const int32_t* sample_start;
+  const int32_t* chunk_gstart;
+  const int32_t* chunk_len;
+  int32_t n_chunk;
+  int64_t n_loc;
+  // forward outputs
+  void* o;
+  bool o_bf16;
+  float* lse;
+  // backward inputs / outputs
+  const void* o_in;
+  const void* dout;
+  const float* lse_in;
+  float* delta;
+  float* dq;
+  void* dk;
+  void* dv;
+  void* dk_self;
+  void* dv_self;
+};
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_fwd_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_delta(const AttnArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_combine(const void* o_parts, bool part_bf16, const float* lse_parts,
+                          int32_t n_parts, int64_t rows, int32_t d, void* o_out, bool out_bf16,
+                          float* lse_out, hipStream_t s);
+// Zero n_words 32-bit words with a fill kernel (no hipMemsetAsync, so the call is
+// safe inside a captured graph).
+hipError_t launch_zero_words(void* p, int64_t n_words, hipStream_t s);
+hipError_t launch_chunk_cost(const int32_t* anchor, const int32_t* sample_start, int32_t n_blk,
+                             int32_t n_ctx, int32_t chunk_size, int64_t* cost, hipStream_t s);
+
+}  // namespace sxa

@@ -1,0 +1,222 @@
+"""ctypes binding of libsxattn (C ABI in include/sxattn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  Tensors are torch tensors on the current HIP device (torch is used for
+device memory and streams); each call is enqueued on torch's current stream.
+The library must have been built (``python -m block_sparse_cross_anchor_amd.build``);
+a missing library raises at the first call -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsxattn.so")
+
+SXA_F32, SXA_BF16 = 0, 1
+SXA_OK, SXA_EINVAL, SXA_EUNSUPPORTED, SXA_EHIP = 0, -1, -2, -3
+BLOCK = 16
+
+EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_bwd", "lse_combine", "chunk_cost", "lpt_assign",
+           "sxa_last_error")
+
+_lib = None
+
+
+class SxaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"sxattn status {status}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsxattn.so and declare the prototypes of every exported entry point."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m block_sparse_cross_anchor_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    attn_common = [P, P, P, ctypes.c_int, I32, I32, I32, I32, I32, F32, P, P, P, P, I32, I64, P, P]
+    lib.sparse_xattn_fwd.argtypes = attn_common + [P, ctypes.c_int, P, P]
+    lib.sparse_xattn_fwd.restype = ctypes.c_int
+    lib.sparse_xattn_bwd.argtypes = attn_common + [P, P, P, P, P, P, P, P, P, P]
+    lib.sparse_xattn_bwd.restype = ctypes.c_int
+    lib.lse_combine.argtypes = [P, ctypes.c_int, P, I32, I64, I32, P, ctypes.c_int, P, P]
+    lib.lse_combine.restype = ctypes.c_int
+    lib.chunk_cost.argtypes = [P, P, I32, I32, I32, I32, P, P]
+    lib.chunk_cost.restype = ctypes.c_int
+    lib.lpt_assign.argtypes = [P, I32, I32, P, P]
+    lib.lpt_assign.restype = ctypes.c_int
+    lib.sxa_last_error.argtypes = []
+    lib.sxa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != SXA_OK:
+        msg = load_library().sxa_last_error().decode(errors="replace")
+        raise SxaError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SXA_BF16
+    if t.dtype == torch.float32:
+        return SXA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+class Meta:
+    """Device metadata of one attention call: per-block anchors and sample starts,
+    and the local chunk list (int32 device tensors)."""
+
+    def __init__(self, anchor, sample_start, chunk_gstart, chunk_len, n_loc=None, device="cuda"):
+        def dev(x):
+            return torch.as_tensor(x, dtype=torch.int32).to(device).contiguous()
+
+        self.anchor = dev(anchor)
+        self.sample_start = dev(sample_start)
+        self.chunk_gstart = dev(chunk_gstart)
+        self.chunk_len = dev(chunk_len)
+        self.n_blk = int(self.anchor.numel())
+        self.n_chunk = int(self.chunk_gstart.numel())
+        self.n_loc = int(torch.as_tensor(chunk_len, dtype=torch.int64).sum()) if n_loc is None \
+            else int(n_loc)
+
+
+def sparse_xattn_fwd(q, k, v, meta: Meta, scale: float, k_self=None, v_self=None,
+                     out_dtype=None, out=None, lse=None):
+    """Partial forward over the local chunks (+ own-block term).  Returns (o, lse)."""
+    n_q, hq, d = q.shape
+    hkv = k.shape[1]
+    _need(q, "q", dtype=q.dtype)
+    _need(k, "k", (meta.n_loc, hkv, d), q.dtype)
+    _need(v, "v", (meta.n_loc, hkv, d), q.dtype)
+    if k_self is not None:
+        _need(k_self, "k_self", (n_q, hkv, d), q.dtype)
+        _need(v_self, "v_self", (n_q, hkv, d), q.dtype)
+    if n_q != meta.n_blk * BLOCK:
+        raise ValueError("q rows must equal 16 * number of blocks")
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((n_q, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((n_q, hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", (n_q, hq, d), out_dtype)
+    _need(lse, "lse", (n_q, hq), torch.float32)
+    lib = load_library()
+    _check(lib.sparse_xattn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), meta.n_blk, BLOCK, hq, hkv, d, float(scale),
+        _ptr(meta.anchor), _ptr(meta.sample_start), _ptr(meta.chunk_gstart), _ptr(meta.chunk_len),
+        meta.n_chunk, meta.n_loc, _ptr(k_self), _ptr(v_self), _ptr(out), _dtype_code(out),
+        _ptr(lse), _stream()))
+    return out, lse
+
+
+def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
+                     k_self=None, v_self=None, delta_ws=None, dk=None, dv=None, dk_self=None,
+                     dv_self=None):
+    """Backward of the local chunks (+ own-block term).  Adds into dq_accum (float32);
+    returns (dk, dv, dk_self, dv_self)."""
+    n_q, hq, d = q.shape
+    hkv = k.shape[1]
+    _need(q, "q")
+    _need(k, "k", (meta.n_loc, hkv, d), q.dtype)
+    _need(v, "v", (meta.n_loc, hkv, d), q.dtype)
+    _need(o, "o", (n_q, hq, d), q.dtype)
+    _need(dout, "dout", (n_q, hq, d), q.dtype)
+    _need(lse, "lse", (n_q, hq), torch.float32)
+    _need(dq_accum, "dq_accum", (n_q, hq, d), torch.float32)
+    if delta_ws is None:
+        delta_ws = torch.empty((n_q, hq), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    if k_self is not None:
+        _need(k_self, "k_self", (n_q, hkv, d), q.dtype)
+        _need(v_self, "v_self", (n_q, hkv, d), q.dtype)
+        if dk_self is None:
+            dk_self = torch.empty_like(k_self)
+        if dv_self is None:
+            dv_self = torch.empty_like(v_self)
+    lib = load_library()
+    _check(lib.sparse_xattn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), meta.n_blk, BLOCK, hq, hkv, d, float(scale),
+        _ptr(meta.anchor), _ptr(meta.sample_start), _ptr(meta.chunk_gstart), _ptr(meta.chunk_len),
+        meta.n_chunk, meta.n_loc, _ptr(k_self), _ptr(v_self), _ptr(o), _ptr(dout), _ptr(lse),
+        _ptr(delta_ws), _ptr(dq_accum), _ptr(dk), _ptr(dv), _ptr(dk_self), _ptr(dv_self),
+        _stream()))
+    return dk, dv, dk_self, dv_self
+
+
+def lse_combine(o_parts, lse_parts, out_dtype=None, out=None, lse_out=None):
+    """o_parts [P, rows, d], lse_parts [P, rows] -> (o [rows, d], lse [rows])."""
+    n_parts, rows, d = o_parts.shape
+    _need(o_parts, "o_parts")
+    _need(lse_parts, "lse_parts", (n_parts, rows), torch.float32)
+    out_dtype = out_dtype or o_parts.dtype
+    if out is None:
+        out = torch.empty((rows, d), dtype=out_dtype, device=o_parts.device)
+    if lse_out is None:
+        lse_out = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
+    _need(out, "out", (rows, d), out_dtype)
+    _need(lse_out, "lse_out", (rows,), torch.float32)
+    lib = load_library()
+    _check(lib.lse_combine(_ptr(o_parts), _dtype_code(o_parts), _ptr(lse_parts), n_parts, rows, d,
+                           _ptr(out), _dtype_code(out), _ptr(lse_out), _stream()))
+    return out, lse_out
+
+
+def chunk_cost(anchor, sample_start, n_ctx: int, chunk_size: int, out=None):
+    """int64 realised cost of every contiguous chunk (device tensor)."""
+    _need(anchor, "anchor", dtype=torch.int32)
+    _need(sample_start, "sample_start", anchor.shape, torch.int32)
+    n_chunk = -(-int(n_ctx) // int(chunk_size)) if chunk_size > 0 else 0
+    if out is None:
+        out = torch.empty((max(n_chunk, 0),), dtype=torch.int64, device=anchor.device)
+    lib = load_library()
+    _check(lib.chunk_cost(_ptr(anchor), _ptr(sample_start), int(anchor.numel()), BLOCK, int(n_ctx),
+                          int(chunk_size), _ptr(out), _stream()))
+    return out
+
+
+def lpt_assign(cost, n_bin: int):
+    """Host LPT plan.  cost: int64 CPU tensor/array.  Returns (bin_of_chunk, bin_load)."""
+    c = torch.as_tensor(cost, dtype=torch.int64).contiguous()
+    if c.is_cuda:
+        raise ValueError("lpt_assign takes host costs")
+    n = int(c.numel())
+    bins = torch.empty((n,), dtype=torch.int32)
+    load = torch.empty((max(int(n_bin), 0),), dtype=torch.int64)
+    lib = load_library()
+    _check(lib.lpt_assign(ctypes.c_void_p(c.data_ptr()), n, int(n_bin),
+                          ctypes.c_void_p(bins.data_ptr()), ctypes.c_void_p(load.data_ptr())))
+    return bins, load

@@ -1,0 +1,158 @@
+/*
+ * sxattn.h - C ABI of libsxattn: anchor-masked block-sparse cross-attention
+ * for one device's share of a packed context, on MI355X (gfx950).
+ *
+ * The operation is the one behind Split-KV context parallelism for training
+ * diffusion drafters ("Split-KV speeds diffusion drafter training by keeping
+ * long-context data local", arXiv 2611.05926):
+ *   - anchors sampled inside each packed sample open blocks of draft tokens;
+ *     every block attends to the preceding context of its own sample and to
+ *     all tokens of its own block (section "Why short queries change the
+ *     problem");
+ *   - keys/values stay local; every query is evaluated against the local
+ *     chunks and the partial results carry normalisation statistics from
+ *     which they are merged exactly (section "Exchange the smaller side");
+ *   - each context chunk gets a cost from its realised attention usage and a
+ *     longest-processing-time-first planner balances chunks across devices
+ *     with equal chunk counts (section "Balance actual attention work").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Block size B is 16 draft tokens.  n_q = n_blk * B queries.
+ * Device tensors are caller-owned, contiguous, token-major:
+ *   q, o, dout, dq_accum : [n_q][hq][d]
+ *   k, v, dk, dv          : [n_loc][hkv][d]   local rows = the listed chunks back to back
+ *   k_self, v_self, dk_self, dv_self : [n_q][hkv][d]  keys/values of the draft tokens
+ *   lse, delta_ws         : [n_q][hq] float32
+ * Query head h reads kv head h / (hq / hkv).
+ * Metadata (device int32 arrays):
+ *   anchor[b], sample_start[b]  global packed positions of block b's anchor and of
+ *                               the start of its sample; block b may attend to
+ *                               context positions j with sample_start[b] <= j < anchor[b]
+ *                               (the anchor itself is excluded);
+ *   chunk_gstart[i], chunk_len[i]  chunk i of the local buffer holds global positions
+ *                               [chunk_gstart[i], chunk_gstart[i] + chunk_len[i]).
+ * The own-block term: query i of block b also attends to rows b*B .. b*B+B-1 of
+ * k_self/v_self (all of them, no causal order).  Pass k_self/v_self on exactly one
+ * call per pass (forward or backward) and NULL on the others.
+ * Logits are scale * <q, k> (scale is a float32 value, usually 1/sqrt(d)); lse is the
+ * natural-log log-sum-exp of the scaled logits.  A row with no allowed key in a call
+ * gets lse = -inf and o = 0.
+ *
+ * Streams and ownership: `stream` is a hipStream_t (NULL = the default stream).
+ * Device work is enqueued asynchronously; outputs are valid after the stream is
+ * synchronised.  The library allocates no device memory; scratch is passed in.
+ *
+ * Errors: every call returns an sxa_status.  Arguments are validated on the host
+ * before anything is enqueued (null pointers, sizes, dtypes, head counts); on a
+ * validation error nothing is launched and outputs are untouched.  A failed launch
+ * returns SXA_EHIP.  sxa_last_error() gives a message for the last failure of the
+ * calling thread.  Metadata values on the device are not validated: anchors must
+ * satisfy sample_start <= anchor, chunks must not overlap, and chunk lengths must
+ * sum to n_loc; other values give unspecified (but in-bounds) results.
+ */
+#ifndef SXATTN_H
+#define SXATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SXA_F32 = 0, SXA_BF16 = 1 } sxa_dtype;
+
+typedef enum {
+  SXA_OK = 0,
+  SXA_EINVAL = -1,        /* bad argument (null pointer, size, dtype, divisibility) */
+  SXA_EUNSUPPORTED = -2,  /* valid but not implemented (head_dim, block size, dtype pair) */
+  SXA_EHIP = -3           /* a HIP runtime call or kernel launch failed */
+} sxa_status;
+
+/*
+ * Partial forward over this call's local chunks (plus the own-block term if
+ * k_self != NULL).  Follows "Why short queries change the problem" (mask) and
+ * "Exchange the smaller side" (local keys/values, partial output with
+ * statistics).
+ *   q [n_q][hq][d], k/v [n_loc][hkv][d] in in_dtype; d in {64, 128}; block_size == 16;
+ *   hq % hkv == 0.  n_chunk >= 0 (0 with k_self set gives the own-block partial alone).
+ *   o [n_q][hq][d] in o_dtype (SXA_F32 or SXA_BF16; SXA_F32 input requires SXA_F32 output),
+ *   lse [n_q][hq] float32.  Both are overwritten.
+ * bf16 inputs run on bf16 MFMA with float32 accumulation and statistics; float32
+ * inputs run in float32 throughout.
+ */
+int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_dtype,
+                     int32_t n_blk, int32_t block_size, int32_t hq, int32_t hkv, int32_t d,
+                     float scale, const int32_t* anchor, const int32_t* sample_start,
+                     const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
+                     int64_t n_loc, const void* k_self, const void* v_self,
+                     void* o, sxa_dtype o_dtype, float* lse, void* stream);
+
+/*
+ * Backward of this call's chunks (and own-block term if k_self != NULL), from the
+ * merged output o, merged lse and upstream gradient dout (all [n_q][hq], dtype
+ * in_dtype for o/dout).  Keys/values stay local: the gradient of the local rows is
+ * produced here ("Exchange the smaller side": local in forward and backward).
+ *   delta_ws [n_q][hq] float32 scratch (overwritten with rowsum(dout * o)).
+ *   dq_accum [n_q][hq][d] float32: this call's query gradient is ADDED to it, so
+ *            per-chunk calls accumulate.
+ *   dk, dv   [n_loc][hkv][d] in in_dtype: overwritten.
+ *   dk_self, dv_self [n_q][hkv][d] in in_dtype: overwritten when k_self != NULL
+ *            (must then be non-NULL), ignored otherwise.
+ */
+int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_dtype,
+                     int32_t n_blk, int32_t block_size, int32_t hq, int32_t hkv, int32_t d,
+                     float scale, const int32_t* anchor, const int32_t* sample_start,
+                     const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
+                     int64_t n_loc, const void* k_self, const void* v_self,
+                     const void* o, const void* dout, const float* lse,
+                     float* delta_ws, float* dq_accum, void* dk, void* dv,
+                     void* dk_self, void* dv_self, void* stream);
+
+/*
+ * Exact merge of n_parts partials from their log-sum-exp statistics
+ * ("Exchange the smaller side": partial results are combined from normalisation
+ * statistics so that the original attention is reconstructed exactly).
+ *   o_parts [n_parts][rows][d] in part_dtype, lse_parts [n_parts][rows] float32
+ *   (rows = n_q * hq for attention partials).  A partial with lse = -inf is skipped
+ *   and its o rows are not read.
+ *   o_out [rows][d] in out_dtype, lse_out [rows] float32: overwritten with
+ *   lse = m + ln(sum_p exp(lse_p - m)), o = sum_p exp(lse_p - lse) o_p; rows whose
+ *   partials are all empty get lse = -inf, o = 0.  d must be 64, 128 or 256.
+ */
+int lse_combine(const void* o_parts, sxa_dtype part_dtype, const float* lse_parts,
+                int32_t n_parts, int64_t rows, int32_t d, void* o_out, sxa_dtype out_dtype,
+                float* lse_out, void* stream);
+
+/*
+ * Realised attention cost of every contiguous context chunk
+ * ("Balance actual attention work": each chunk is costed from its actual
+ * attention usage, computable from the global query view).
+ *   cost_out[c] (device int64, c < ceil(n_ctx / chunk_size)) = number of
+ *   (query token, key) pairs with the key in [c*chunk_size, min((c+1)*chunk_size, n_ctx))
+ *   allowed by the anchor mask, for one head; own-block pairs are not counted.
+ *   Exact integer result.
+ */
+int chunk_cost(const int32_t* anchor, const int32_t* sample_start, int32_t n_blk,
+               int32_t block_size, int32_t n_ctx, int32_t chunk_size, int64_t* cost_out,
+               void* stream);
+
+/*
+ * Longest-processing-time-first assignment of chunks to n_bin devices with equal
+ * chunk counts ("Balance actual attention work").  HOST pointers, synchronous.
+ *   cost[n_chunk] int64 >= 0; n_chunk must be a positive multiple of n_bin.
+ *   Chunks are taken by (cost descending, index ascending); each goes to the bin
+ *   with the smallest (load, bin index) among bins holding fewer than n_chunk/n_bin
+ *   chunks.  bin_of_chunk[n_chunk] and bin_load[n_bin] are overwritten.
+ */
+int lpt_assign(const int64_t* cost, int32_t n_chunk, int32_t n_bin, int32_t* bin_of_chunk,
+               int64_t* bin_load);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* sxa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SXATTN_H */

@@ -1,0 +1,95 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports every
+entry point declared in include/sxattn.h, rejects bad arguments before touching
+the device, and its host LPT planner is bit-identical to the oracle's."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from block_sparse_cross_anchor_amd import sxattn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sxattn.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sxattn.LIB_PATH):
+        pytest.skip("libsxattn.so not built")
+    return sxattn.load_library()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_symbols() == sorted(sxattn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_invalid_arguments_are_rejected_on_the_host(lib):
+    null = None
+    # block size other than 16
+    st_ = lib.chunk_cost(null, null, 1, 8, 100, 10, null, null)
+    assert st_ == sxattn.SXA_EUNSUPPORTED
+    assert b"block_size" in lib.sxa_last_error()
+    # chunk size 0
+    assert lib.chunk_cost(null, null, 0, 16, 100, 0, null, null) == sxattn.SXA_EINVAL
+    # LPT: counts not divisible
+    cost = (ctypes.c_int64 * 3)(1, 2, 3)
+    bins = (ctypes.c_int32 * 3)()
+    load = (ctypes.c_int64 * 2)()
+    assert lib.lpt_assign(cost, 3, 2, bins, load) == sxattn.SXA_EINVAL
+    # attention: head_dim 96 unsupported, hq not a multiple of hkv, bad scale
+    args = [null, null, null, 1, 1, 16, 4, 2, 96, 0.1, null, null, null, null, 0, 0, null, null,
+            null, 1, null, null]
+    assert lib.sparse_xattn_fwd(*args) == sxattn.SXA_EUNSUPPORTED
+    args[8], args[6], args[7] = 128, 6, 4
+    assert lib.sparse_xattn_fwd(*args) == sxattn.SXA_EINVAL
+    args[6], args[7], args[9] = 4, 2, -1.0
+    assert lib.sparse_xattn_fwd(*args) == sxattn.SXA_EINVAL
+    # float32 in, bf16 out
+    args[9], args[19] = 0.1, sxattn.SXA_BF16
+    args[3], args[4] = sxattn.SXA_F32, 0
+    assert lib.sparse_xattn_fwd(*args) == sxattn.SXA_EUNSUPPORTED
+    # combine: unsupported d
+    assert lib.lse_combine(null, 1, null, 1, 10, 96, null, 1, null, null) == sxattn.SXA_EUNSUPPORTED
+    # a good call clears the message
+    assert lib.lpt_assign((ctypes.c_int64 * 2)(1, 2), 2, 2, (ctypes.c_int32 * 2)(),
+                          (ctypes.c_int64 * 2)()) == sxattn.SXA_OK
+    assert lib.sxa_last_error() == b""
+
+
+def test_lpt_golden(lib):
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "lpt_tiny.json")))
+    for case in g["cases"]:
+        bins, load = sxattn.lpt_assign(np.asarray(case["cost"], np.int64), case["n_bin"])
+        assert bins.tolist() == case["bin_of_chunk"] and load.tolist() == case["bin_load"]
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.integers(1, 16), st.integers(1, 12),
+       st.lists(st.integers(0, 40), min_size=1, max_size=400), st.booleans())
+def test_lpt_matches_oracle_bit_exact(lib, n_bin, per_bin, pool, wide):
+    n = n_bin * per_bin
+    cost = np.resize(np.asarray(pool, np.int64), n)
+    if wide:
+        cost = cost * np.int64(3_000_000_007)  # beyond int32
+    want_bins, want_load = oracle.lpt_assign(cost, n_bin)
+    bins, load = sxattn.lpt_assign(cost, n_bin)
+    assert bins.tolist() == want_bins
+    assert load.tolist() == want_load
