@@ -42,9 +42,8 @@
 namespace sxa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerWG = 256;
 constexpr int kTileKeys = 64;
+constexpr float kRescaleSlack = 8.f;  // log2 units
 
 struct FwdParams {
   const uint16_t* q;
@@ -124,68 +123,85 @@ __device__ __forceinline__ int vt_pos(int key) {
 }
 __device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
 
-template <int D>
+// Staging of one 64-key tile (K and V rows of one kv head) through registers into
+// LDS, split over all T threads of the workgroup.  K is stored row-major with the
+// 16-byte chunk index XOR-ed by (key & 7); V is stored transposed (one 64-key row
+// per head-dim element) with the key order permuted by vt_pos and the 16-byte
+// chunks XOR-ed by vt_swz(d).
+template <int D, int T>
 struct TileRegs {
-  static constexpr int CPR = D / 8;                       // 16-byte chunks per row
-  static constexpr int KLOADS = kTileKeys * CPR / kThreads;  // K chunks per thread
-  static constexpr int VITEMS = kTileKeys / 4 * CPR;         // (key quad, chunk) items
-  u32x4 k[KLOADS];
-  u32x4 v[4];
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int KCH = kTileKeys * CPR;     // K chunks per tile
+  static constexpr int VIT = kTileKeys / 2 * CPR; // V items: (key pair, chunk)
+  static constexpr int KL = (KCH + T - 1) / T;
+  static constexpr int VL = (VIT + T - 1) / T;
+  u32x4 k[KL];
+  u32x4 v[VL][2];
 
+  // Rows past the tile end are clamped to its last row: those keys are masked, so
+  // any finite value will do and the loads stay branch-free.
   __device__ __forceinline__ void load(const Tile& t, const FwdParams& p, int g, int tid) {
     const uint16_t* K = t.self ? p.k_self : p.k;
     const uint16_t* V = t.self ? p.v_self : p.v;
+    const int last = t.nrows - 1;
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int idx = tid + kThreads * i;
-      const int key = idx / CPR, j = idx % CPR;
-      if (key < t.nrows)
+    for (int i = 0; i < KL; ++i) {
+      const int idx = tid + T * i;
+      if (KCH % T == 0 || idx < KCH) {
+        const int key = min(idx / CPR, last), j = idx % CPR;
         k[i] = *reinterpret_cast<const u32x4*>(K + ((t.row0 + key) * p.hkv + g) * D + 8 * j);
-      else
-        k[i] = u32x4{0, 0, 0, 0};
+      }
     }
-    if (tid < VITEMS) {
-      const int q4 = tid / CPR, j = tid % CPR;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = 4 * q4 + kk;
-        if (key < t.nrows)
-          v[kk] = *reinterpret_cast<const u32x4*>(V + ((t.row0 + key) * p.hkv + g) * D + 8 * j);
-        else
-          v[kk] = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < VL; ++i) {
+      const int it = tid + T * i;
+      if (VIT % T == 0 || it < VIT) {
+        const int q2 = it / CPR, j = it % CPR;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int key = min(2 * q2 + kk, last);
+          v[i][kk] = *reinterpret_cast<const u32x4*>(V + ((t.row0 + key) * p.hkv + g) * D + 8 * j);
+        }
       }
     }
   }
 
   __device__ __forceinline__ void store(uint16_t* lk, uint16_t* lv, int tid) const {
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int idx = tid + kThreads * i;
-      const int key = idx / CPR, j = idx % CPR;
-      *reinterpret_cast<u32x4*>(lk + key * D + 8 * (j ^ (key & 7))) = k[i];
+    for (int i = 0; i < KL; ++i) {
+      const int idx = tid + T * i;
+      if (KCH % T == 0 || idx < KCH) {
+        const int key = idx / CPR, j = idx % CPR;
+        *reinterpret_cast<u32x4*>(lk + key * D + 8 * (j ^ (key & 7))) = k[i];
+      }
     }
-    if (tid < VITEMS) {
-      const int q4 = tid / CPR, j = tid % CPR;
-      const int pos = vt_pos(4 * q4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * j + e;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(v[1][e >> 1], v[0][e >> 1], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(v[3][e >> 1], v[2][e >> 1], sel);
-        const int phys = ((pos >> 3) ^ vt_swz(d));
-        *reinterpret_cast<u32x2*>(lv + d * kTileKeys + 8 * phys + (pos & 7)) = u32x2{lo, hi};
+    for (int i = 0; i < VL; ++i) {
+      const int it = tid + T * i;
+      if (VIT % T == 0 || it < VIT) {
+        const int q2 = it / CPR, j = it % CPR;
+        const int pos = vt_pos(2 * q2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 8 * j + e;
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t w = __builtin_amdgcn_perm(v[i][1][e >> 1], v[i][0][e >> 1], sel);
+          const int phys = (pos >> 3) ^ vt_swz(d);
+          *reinterpret_cast<uint32_t*>(lv + d * kTileKeys + 8 * phys + (pos & 7)) = w;
+        }
       }
     }
   }
 };
 
-template <int D, bool OUT_BF16>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1))) void
+// NT: 32-row N tiles per wave (rows per wave = 32 * NT); WAVES: waves per workgroup.
+template <int D, int NT, int WAVES, bool OUT_BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES))) void
 fwd_bf16_kernel(FwdParams p) {
-  constexpr int KS = D / 16;  // k-steps of S^T
-  constexpr int DT = D / 32;  // 32-row d tiles of O^T
+  constexpr int T = 64 * WAVES;
+  constexpr int ROWS = 32 * NT * WAVES;  // rows per workgroup
+  constexpr int KS = D / 16;             // k-steps of S^T
+  constexpr int DT = D / 32;             // 32-row d tiles of O^T
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileKeys * D];
 
   const int tid = threadIdx.x;
@@ -194,8 +210,8 @@ fwd_bf16_kernel(FwdParams p) {
   const int wg = blockIdx.x / p.hkv;
   const int grp = p.hq / p.hkv;
   const int64_t R = static_cast<int64_t>(p.n_blk) * kBlock * grp;
-  const int64_t wg_row0 = static_cast<int64_t>(wg) * kRowsPerWG;
-  const int64_t wg_last = min(wg_row0 + kRowsPerWG - 1, R - 1);
+  const int64_t wg_row0 = static_cast<int64_t>(wg) * ROWS;
+  const int64_t wg_last = min(wg_row0 + ROWS - 1, R - 1);
   const int b_first = static_cast<int>(wg_row0 / grp / kBlock);
   const int b_last = static_cast<int>(wg_last / grp / kBlock);
   int LO = 0x7fffffff, HI = -0x7fffffff;
@@ -205,13 +221,13 @@ fwd_bf16_kernel(FwdParams p) {
   }
 
   // per-lane query columns (one per 32-row N tile)
-  int clo[2], chi[2], slo[2], shi[2];
-  int64_t orow[2];
-  bool valid[2];
-  bf16x8 qf[2][KS];
+  int clo[NT], chi[NT], slo[NT], shi[NT];
+  int64_t orow[NT];
+  bool valid[NT];
+  bf16x8 qf[NT][KS];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int64_t r = wg_row0 + 64 * wave + 32 * nt + l32;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t r = wg_row0 + 32 * NT * wave + 32 * nt + l32;
     valid[nt] = r < R;
     const int64_t rr = valid[nt] ? r : 0;
     const int64_t tok = rr / grp;
@@ -224,8 +240,7 @@ fwd_bf16_kernel(FwdParams p) {
     orow[nt] = tok * p.hq + static_cast<int64_t>(g) * grp + hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 raw = u32x4{0, 0, 0, 0};
-      if (valid[nt]) raw = *reinterpret_cast<const u32x4*>(p.q + orow[nt] * D + 16 * ks + 8 * h2);
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(p.q + orow[nt] * D + 16 * ks + 8 * h2);
       qf[nt][ks] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -237,17 +252,20 @@ fwd_bf16_kernel(FwdParams p) {
   w.off = 0;
   w.gs = w.len = w.t = w.t_end = 0;
 
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  f32x16 oacc[DT][2];
+  float m[NT], l[NT];
+  f32x16 oacc[DT][NT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = -INFINITY;
+    l[nt] = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[dt][nt][r] = 0.f;
+  }
 
   Tile cur, nxt;
-  TileRegs<D> regs;
+  TileRegs<D, T> regs;
   bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
   if (have) {
     regs.load(cur, p, g, tid);
@@ -260,10 +278,10 @@ fwd_bf16_kernel(FwdParams p) {
     if (has_next) regs.load(nxt, p, g, tid);
 
     // ---- this wave's share of the tile
-    int a_lo[2], a_hi[2];
+    int a_lo[NT], a_hi[NT];
     bool any = false, full = true;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const int lo = cur.self ? slo[nt] : clo[nt];
       const int hi = cur.self ? shi[nt] : chi[nt];
       a_lo[nt] = max(lo - cur.coord0, 0);
@@ -275,11 +293,11 @@ fwd_bf16_kernel(FwdParams p) {
       const bool all_full = __all(full);
       const uint16_t* lk = lds[buf][0];
       const uint16_t* lv = lds[buf][1];
-      f32x16 sacc[2][2];
+      f32x16 sacc[2][NT];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[mt][nt][r] = 0.f;
 #pragma unroll
@@ -290,13 +308,16 @@ fwd_bf16_kernel(FwdParams p) {
           const bf16x8 kf = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(lk + key * D + 8 * ((2 * ks + h2) ^ (key & 7))));
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
             sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], sacc[mt][nt], 0, 0, 0);
         }
       }
-      bf16x8 pf[2][4];
+      bf16x8 pf[NT][4];
+      bool need[NT];
+      float tmax[NT];
+      bool any_need = false;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         if (!all_full) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
@@ -311,25 +332,41 @@ fwd_bf16_kernel(FwdParams p) {
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const float mnew = fmaxf(m[nt], mx * p.scale_log2);
-        const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = exp2f(m[nt] - muse);
+        mx = fmaxf(mx, swap_halves(mx)) * p.scale_log2;
+        need[nt] = mx > m[nt] + kRescaleSlack;
+        tmax[nt] = mx;
+        any_need |= need[nt];
+      }
+      // Lazy rescale: the running max of a column only moves when the tile max
+      // exceeds it by more than kRescaleSlack (so p <= 2^kRescaleSlack); the O
+      // accumulators are rescaled only then, for the whole wave at once.
+      if (__any(any_need)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float mnew = need[nt] ? tmax[nt] : m[nt];
+          const float alpha =
+              need[nt] ? (m[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[nt] - mnew)) : 1.f;
+          m[nt] = mnew;
+          l[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float muse = m[nt] == -INFINITY ? 0.f : m[nt];
         float rs = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float e = exp2f(fmaf(sacc[mt][nt][r], p.scale_log2, -muse));
+            const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], p.scale_log2, -muse));
             sacc[mt][nt][r] = e;
             rs += e;
           }
-        l[nt] = fmaf(l[nt], alpha, rs);
-        m[nt] = mnew;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
+        l[nt] += rs;
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
@@ -344,7 +381,7 @@ fwd_bf16_kernel(FwdParams p) {
           const bf16x8 vf = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(lv + d * kTileKeys + 8 * ((2 * kq + h2) ^ vt_swz(d))));
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
             oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nt][kq], oacc[dt][nt], 0, 0, 0);
         }
       }
@@ -359,7 +396,7 @@ fwd_bf16_kernel(FwdParams p) {
 
   // ---- epilogue: normalise, write O and lse
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const float lt = l[nt] + swap_halves(l[nt]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (!valid[nt]) continue;
@@ -384,6 +421,10 @@ fwd_bf16_kernel(FwdParams p) {
   }
 }
 
+constexpr int kNT = 1;      // 32 query rows per wave
+constexpr int kWaves = 8;   // 8 waves (2 per SIMD) share each K/V tile
+constexpr int kRowsPerWG = 32 * kNT * kWaves;
+
 template <int D, bool OUT_BF16>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   FwdParams p;
@@ -407,7 +448,8 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   const int64_t groups = (rows + kRowsPerWG - 1) / kRowsPerWG;
   const int64_t n_wg = groups * a.hkv;
   if (n_wg == 0) return hipSuccess;
-  fwd_bf16_kernel<D, OUT_BF16><<<dim3(static_cast<unsigned>(n_wg)), dim3(kThreads), 0, s>>>(p);
+  fwd_bf16_kernel<D, kNT, kWaves, OUT_BF16>
+      <<<dim3(static_cast<unsigned>(n_wg)), dim3(64 * kWaves), 0, s>>>(p);
   return hipGetLastError();
 }
 
