@@ -1,0 +1,193 @@
+"""GPU parity of the backward path against the CPU oracle.
+
+The backward takes the merged output O and log-sum-exp as inputs, so both sides
+receive the same O/lse bits (produced here by the GPU forward) and the same dO.
+Tolerances: bf16 gradients relative Frobenius <= 3e-2; float32 gradients 1e-5.
+At the 4096-query x 32768-context shape the oracle evaluates sampled blocks (for
+dQ) and sampled key rows (for dK/dV, as a one-chunk call over all blocks); every
+gradient entry of those depends only on the inputs, O, lse and dO.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_cross_anchor_amd import synth, sxattn
+from helpers import dev, device_meta, host64, rel_frob, sub_blocks, token_rows
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+W = synth.WORKLOADS
+
+
+def gpu_fwd_merged(meta, inp, scale, dm):
+    """Unsplit GPU forward: the merged O (in_dtype) and lse that the backward consumes."""
+    o, lse = sxattn.sparse_xattn_fwd(dev(inp.q), dev(inp.k), dev(inp.v), dm, scale,
+                                     dev(inp.k_self), dev(inp.v_self))
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def run_case(meta, inp, scale, gs, gl, tol, dq_init=None):
+    dm = device_meta(meta, gs, gl)
+    o, lse = gpu_fwd_merged(meta, inp, scale, dm)
+    dq = torch.zeros(inp.q.shape, dtype=torch.float32, device="cuda") if dq_init is None \
+        else dq_init.clone()
+    dk, dv, dks, dvs = sxattn.sparse_xattn_bwd(dev(inp.q), dev(inp.k), dev(inp.v), dm, scale, o,
+                                               dev(inp.dout), lse, dq, dev(inp.k_self),
+                                               dev(inp.v_self))
+    torch.cuda.synchronize()
+    r = oracle.sparse_xattn_bwd(inp.q.f64, inp.k.f64, inp.v.f64, host64(o), inp.dout.f64,
+                                host64(lse), meta.anchor, meta.sample_start, gs, gl, scale,
+                                inp.k_self.f64, inp.v_self.f64)
+    want_dq = r[0] if dq_init is None else r[0] + host64(dq_init)
+    for got, want, name in ((dq, want_dq, "dq"), (dk, r[1], "dk"), (dv, r[2], "dv"),
+                            (dks, r[3], "dk_self"), (dvs, r[4], "dv_self")):
+        err = rel_frob(host64(got), want)
+        assert err <= tol, f"{name}: relative Frobenius error {err:.3e} > {tol}"
+    return o, lse
+
+
+@pytest.mark.parametrize("seed", [1, 101])
+def test_bwd_bf16_4k_unsplit(seed):
+    w = W["fwd_bf16_512q_4k"]
+    gs, gl = synth.contiguous_chunks(w.n_ctx, w.chunk_size)
+    meta = synth.meta_for(w, seed)
+    inp = synth.draw_inputs(seed, meta, w.hq, w.hkv, w.d, "bf16", w.std(), gs, gl,
+                            with_dout=True)
+    run_case(meta, inp, 1.0 / math.sqrt(w.d), gs, gl, 3e-2)
+
+
+@pytest.mark.parametrize("seed", [2, 3])
+def test_bwd_bf16_sharp_ragged_chunks_and_dq_accumulation(seed):
+    """N(0,1) values, chunk edges off the tile grid, chunks out of order, and dq_accum
+    holding earlier contributions (the call adds to it)."""
+    w = W["fwd_bf16_512q_4k"]
+    rng = np.random.default_rng(seed)
+    cuts = np.sort(rng.choice(np.arange(1, w.n_ctx), size=7, replace=False))
+    starts = np.concatenate([[0], cuts]).astype(np.int32)
+    lens = np.diff(np.concatenate([starts, [w.n_ctx]])).astype(np.int32)
+    perm = rng.permutation(len(starts))
+    gs, gl = starts[perm], lens[perm]
+    meta = synth.meta_for(w, seed)
+    inp = synth.draw_inputs(seed, meta, w.hq, w.hkv, w.d, "bf16", 1.0, gs, gl, with_dout=True)
+    dq0 = torch.randn(inp.q.shape, dtype=torch.float32, device="cuda",
+                      generator=torch.Generator(device="cuda").manual_seed(seed))
+    run_case(meta, inp, 1.0 / math.sqrt(w.d), gs, gl, 3e-2, dq_init=dq0)
+
+
+def test_bwd_bf16_gqa_and_head_dim_variants():
+    for hq, hkv, d in [(4, 4, 64), (8, 4, 128), (16, 2, 128), (4, 2, 64)]:
+        meta = synth.draw_meta(8, 3000, 300, 1200, 12)
+        gs, gl = synth.contiguous_chunks(3000, 700)
+        inp = synth.draw_inputs(8, meta, hq, hkv, d, "bf16", 1.0, gs, gl, with_dout=True)
+        run_case(meta, inp, 1.0 / math.sqrt(d), gs, gl, 3e-2)
+
+
+def test_bwd_fp32_tiny():
+    w = W["tiny_fp32_512"]
+    gs, gl = synth.contiguous_chunks(w.n_ctx, w.chunk_size)
+    meta = synth.meta_for(w, 4)
+    inp = synth.draw_inputs(4, meta, w.hq, w.hkv, w.d, "f32", 1.0, gs, gl, with_dout=True)
+    run_case(meta, inp, 1.0 / math.sqrt(w.d), gs, gl, 1e-5)
+
+
+def test_bwd_per_chunk_calls_sum_to_unsplit():
+    """One call per chunk (own-block term on the first), dq accumulated across calls,
+    equals the oracle's unsplit backward."""
+    w = W["fwd_bf16_512q_4k"]
+    gs, gl = synth.contiguous_chunks(w.n_ctx, w.chunk_size)
+    meta = synth.meta_for(w, 9)
+    inp = synth.draw_inputs(9, meta, w.hq, w.hkv, w.d, "bf16", 1.0, gs, gl, with_dout=True)
+    scale = 1.0 / math.sqrt(w.d)
+    o, lse = gpu_fwd_merged(meta, inp, scale, device_meta(meta, gs, gl))
+    q, k, v, do = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.dout)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+    offs = np.concatenate([[0], np.cumsum(gl)])
+    dks = []
+    for c in range(len(gs)):
+        dm = device_meta(meta, gs[c:c + 1], gl[c:c + 1])
+        sl = slice(int(offs[c]), int(offs[c + 1]))
+        dk, dv, dk_s, dv_s = sxattn.sparse_xattn_bwd(
+            q, k[sl].contiguous(), v[sl].contiguous(), dm, scale, o, do, lse, dq,
+            dev(inp.k_self) if c == 0 else None, dev(inp.v_self) if c == 0 else None)
+        dks.append((dk, dv, dk_s, dv_s))
+    torch.cuda.synchronize()
+    r = oracle.sparse_xattn_bwd(inp.q.f64, inp.k.f64, inp.v.f64, host64(o), inp.dout.f64,
+                                host64(lse), meta.anchor, meta.sample_start, gs, gl, scale,
+                                inp.k_self.f64, inp.v_self.f64)
+    assert rel_frob(host64(dq), r[0]) <= 3e-2
+    dk_all = np.concatenate([host64(x[0]) for x in dks])
+    dv_all = np.concatenate([host64(x[1]) for x in dks])
+    assert rel_frob(dk_all, r[1]) <= 3e-2
+    assert rel_frob(dv_all, r[2]) <= 3e-2
+    assert rel_frob(host64(dks[0][2]), r[3]) <= 3e-2
+    assert rel_frob(host64(dks[0][3]), r[4]) <= 3e-2
+
+
+def test_bwd_no_queries_zero_gradients():
+    k = torch.randn(100, 2, 128, device="cuda").to(torch.bfloat16)
+    dm = sxattn.Meta(np.zeros(0, np.int32), np.zeros(0, np.int32), [0], [100])
+    q = torch.zeros(0, 4, 128, device="cuda", dtype=torch.bfloat16)
+    dq = torch.zeros(0, 4, 128, device="cuda")
+    lse = torch.zeros(0, 4, device="cuda")
+    dk, dv, _, _ = sxattn.sparse_xattn_bwd(q, k, k, dm, 0.1, q, q, lse, dq,
+                                           dk=torch.full_like(k, 3.0), dv=torch.full_like(k, 3.0))
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_bwd_4k_queries_32k_context_per_chunk_sampled():
+    """4096 queries x 32768 context, GQA 32/8, d = 128, 8 chunks of 4096 with one
+    backward call each (the layout of one device's chunks); dq accumulated over the
+    calls.  Sampled blocks (dq) and sampled key rows (dk, dv) against the oracle."""
+    w = W["fwdbwd_bf16_4kq_32k"]
+    gs, gl = synth.contiguous_chunks(w.n_ctx, w.chunk_size)
+    meta = synth.meta_for(w, 4)
+    inp = synth.draw_inputs(4, meta, w.hq, w.hkv, w.d, "bf16", w.std(), gs, gl, with_dout=True)
+    scale = 1.0 / math.sqrt(w.d)
+    o, lse = gpu_fwd_merged(meta, inp, scale, device_meta(meta, gs, gl))
+    q, k, v, do = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.dout)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    offs = np.concatenate([[0], np.cumsum(gl)])
+    dks = dvs = None
+    for c in range(len(gs)):
+        dm = device_meta(meta, gs[c:c + 1], gl[c:c + 1])
+        sl = slice(int(offs[c]), int(offs[c + 1]))
+        dk_c, dv_c, dks_c, dvs_c = sxattn.sparse_xattn_bwd(
+            q, k[sl].contiguous(), v[sl].contiguous(), dm, scale, o, do, lse, dq,
+            dev(inp.k_self) if c == 0 else None, dev(inp.v_self) if c == 0 else None)
+        dk[sl] = dk_c
+        dv[sl] = dv_c
+        if c == 0:
+            dks, dvs = dks_c, dvs_c
+    torch.cuda.synchronize()
+    o64, lse64 = host64(o), host64(lse)
+    # dq of sampled blocks: every allowed key of those blocks over all chunks
+    rng = np.random.default_rng(1)
+    blocks = np.unique(np.concatenate([[0, meta.n_blk - 1], rng.integers(0, meta.n_blk, 6)]))
+    sub = sub_blocks(meta, blocks)
+    rows = token_rows(blocks)
+    r = oracle.sparse_xattn_bwd(inp.q.f64[rows], inp.k.f64, inp.v.f64, o64[rows],
+                                inp.dout.f64[rows], lse64[rows], sub.anchor, sub.sample_start,
+                                gs, gl, scale, inp.k_self.f64[rows], inp.v_self.f64[rows])
+    assert rel_frob(host64(dq)[rows], r[0]) <= 3e-2
+    assert rel_frob(host64(dks)[rows], r[3]) <= 3e-2
+    assert rel_frob(host64(dvs)[rows], r[4]) <= 3e-2
+    # dk, dv of sampled key rows: a one-chunk oracle call over all blocks
+    for start in rng.integers(0, w.n_ctx - 64, 3):
+        start = int(start)
+        g1, l1 = np.array([start], np.int32), np.array([64], np.int32)
+        rr = oracle.sparse_xattn_bwd(inp.q.f64, inp.k.f64[start:start + 64],
+                                     inp.v.f64[start:start + 64], o64, inp.dout.f64, lse64,
+                                     meta.anchor, meta.sample_start, g1, l1, scale)
+        if np.abs(rr[1]).max() == 0:
+            continue
+        assert rel_frob(host64(dk)[start:start + 64], rr[1]) <= 3e-2
+        assert rel_frob(host64(dv)[start:start + 64], rr[2]) <= 3e-2
