@@ -120,16 +120,22 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                      const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
                      int64_t n_loc, const void* k_self, const void* v_self, const void* o,
                      const void* dout, const float* lse, float* delta_ws, float* dq_accum,
-                     void* dk, void* dv, void* dk_self, void* dv_self, void* stream) {
+                     void* dk, void* dv, void* dk_self, void* dv_self, int32_t flags,
+                     void* stream) {
   sxa::AttnArgs a;
   int st = check_attn(q, k, v, in_dtype, n_blk, block_size, hq, hkv, d, scale, anchor,
                       sample_start, chunk_gstart, chunk_len, n_chunk, n_loc, k_self, v_self, a);
   if (st != SXA_OK) return st;
-  if (n_blk > 0 && (o == nullptr || dout == nullptr || lse == nullptr || delta_ws == nullptr ||
-                    dq_accum == nullptr))
-    return fail(SXA_EINVAL, "o, dout, lse, delta_ws and dq_accum must not be NULL");
-  if (n_loc > 0 && (dk == nullptr || dv == nullptr)) return fail(SXA_EINVAL, "dk and dv must not be NULL");
-  if (k_self != nullptr && (dk_self == nullptr || dv_self == nullptr))
+  constexpr int32_t kAll = SXA_BWD_DELTA | SXA_BWD_DQ | SXA_BWD_DKDV;
+  if (flags == 0) flags = kAll;
+  if (flags & ~(kAll | SXA_BWD_DQ_OVERWRITE)) return fail(SXA_EINVAL, "unknown flags 0x%x", flags);
+  if (n_blk > 0 && (o == nullptr || dout == nullptr || lse == nullptr || delta_ws == nullptr))
+    return fail(SXA_EINVAL, "o, dout, lse and delta_ws must not be NULL");
+  if (n_blk > 0 && (flags & SXA_BWD_DQ) && dq_accum == nullptr)
+    return fail(SXA_EINVAL, "dq_accum must not be NULL");
+  if ((flags & SXA_BWD_DKDV) && n_loc > 0 && (dk == nullptr || dv == nullptr))
+    return fail(SXA_EINVAL, "dk and dv must not be NULL");
+  if ((flags & SXA_BWD_DKDV) && k_self != nullptr && (dk_self == nullptr || dv_self == nullptr))
     return fail(SXA_EINVAL, "dk_self and dv_self must not be NULL when k_self is given");
   a.o_in = o;
   a.dout = dout;
@@ -140,8 +146,10 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
   a.dv = dv;
   a.dk_self = dk_self;
   a.dv_self = dv_self;
+  a.flags = flags;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_blk == 0) {
+    if (!(flags & SXA_BWD_DKDV)) return ok();
     // no query: the gradients of the local keys/values are zero
     const int64_t es = in_dtype == SXA_BF16 ? 2 : 4;
     const int64_t kv_words = n_loc * hkv * d * es / 4;
@@ -189,6 +197,22 @@ int chunk_cost(const int32_t* anchor, const int32_t* sample_start, int32_t n_blk
   return hip_status(sxa::launch_chunk_cost(anchor, sample_start, n_blk, n_ctx, chunk_size, cost_out,
                                            static_cast<hipStream_t>(stream)),
                     "chunk_cost launch");
+}
+
+int context_gather(const void* src, int64_t row_bytes, const int32_t* chunk_gstart,
+                   const int32_t* chunk_len, int32_t n_chunk, int64_t n_dst_rows, void* dst,
+                   void* stream) {
+  if (row_bytes <= 0 || row_bytes % 16 != 0)
+    return fail(SXA_EINVAL, "row_bytes must be a positive multiple of 16 (got %lld)",
+                static_cast<long long>(row_bytes));
+  if (n_chunk < 0 || n_dst_rows < 0) return fail(SXA_EINVAL, "n_chunk and n_dst_rows must be >= 0");
+  if (n_chunk > 0 && (chunk_gstart == nullptr || chunk_len == nullptr))
+    return fail(SXA_EINVAL, "chunk_gstart and chunk_len must not be NULL");
+  if (n_dst_rows > 0 && (src == nullptr || dst == nullptr)) return fail(SXA_EINVAL, "src and dst must not be NULL");
+  if (n_chunk == 0 || n_dst_rows == 0) return ok();
+  return hip_status(sxa::launch_context_gather(src, row_bytes, chunk_gstart, chunk_len, n_chunk, n_dst_rows,
+                                               dst, static_cast<hipStream_t>(stream)),
+                    "context_gather launch");
 }
 
 int lpt_assign(const int64_t* cost, int32_t n_chunk, int32_t n_bin, int32_t* bin_of_chunk,

@@ -52,6 +52,7 @@ struct BwdParams {
   int32_t n_blk, hq, hkv, n_chunk;
   float scale;
   float scale_log2;  // scale * log2(e)
+  int32_t dq_overwrite;
 };
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
@@ -216,6 +217,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
     HI = max(HI, p.anchor[b]);
   }
 
+  Walk w;
+  w.self_pos = p.k_self ? kBlock * b_first : 0;
+  w.self_end = p.k_self ? kBlock * (b_last + 1) : 0;
+  w.c = -1;
+  w.off = 0;
+  w.gs = w.len = w.t = w.t_end = 0;
+  Tile cur, nxt;
+  bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
+
   // this lane's query row (column of the 32-row N tile)
   const int64_t r = wg_row0 + 32 * wave + l32;
   const bool valid = r < R;
@@ -223,9 +233,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
   const int64_t tok = rr / grp;
   const int hh = static_cast<int>(rr % grp);
   const int blk = static_cast<int>(tok / kBlock);
+  const int64_t orow = tok * p.hq + static_cast<int64_t>(g) * grp + hh;
+  if (!have) {  // no key of this call reaches these rows: nothing to add
+    if (p.dq_overwrite && valid) {
+      // the two lanes of a row (h2 = 0, 1) each clear half of it
+#pragma unroll
+      for (int d0 = h2 * (D / 2); d0 < (h2 + 1) * (D / 2); d0 += 4)
+        *reinterpret_cast<f32x4*>(p.dq + orow * D + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
   const int clo = valid ? p.sample_start[blk] : 0, chi = valid ? p.anchor[blk] : 0;
   const int slo = valid ? kBlock * blk : 0, shi = valid ? kBlock * blk + kBlock : 0;
-  const int64_t orow = tok * p.hq + static_cast<int64_t>(g) * grp + hh;
   const float lse_nat = p.lse[orow];
   // rows with no key at all contribute nothing: exp2(x - inf) = 0
   const float lse2 = (valid && lse_nat != -INFINITY) ? lse_nat * kLog2e : INFINITY;
@@ -237,27 +256,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
     df[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p.dout + orow * D + 16 * ks + 8 * h2));
   }
 
-  Walk w;
-  w.self_pos = p.k_self ? kBlock * b_first : 0;
-  w.self_end = p.k_self ? kBlock * (b_last + 1) : 0;
-  w.c = -1;
-  w.off = 0;
-  w.gs = w.len = w.t = w.t_end = 0;
-
   f32x16 dqacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[dt][i] = 0.f;
 
-  Tile cur, nxt;
   DqTileRegs<D> regs;
-  bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
-  if (have) {
-    regs.load(cur, p, g, tid);
-    regs.store(lds[0][0], lds[0][1], lds[0][2], tid);
-    __syncthreads();
-  }
+  regs.load(cur, p, g, tid);
+  regs.store(lds[0][0], lds[0][1], lds[0][2], tid);
+  __syncthreads();
   int buf = 0;
   while (have) {
     const bool has_next = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, nxt);
@@ -327,7 +335,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       float* dst = p.dq + orow * D + 32 * dt + 8 * jj + 4 * h2;
-      f32x4 acc = *reinterpret_cast<const f32x4*>(dst);
+      f32x4 acc = p.dq_overwrite ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(dst);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(p.scale, dqacc[dt][4 * jj + i], acc[i]);
       *reinterpret_cast<f32x4*>(dst) = acc;
@@ -618,8 +626,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dkdv_bf16_k
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
-  hipError_t e = launch_delta(a, true, s);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (a.flags & SXA_BWD_DELTA) {
+    if ((e = launch_delta(a, true, s)) != hipSuccess) return e;
+  }
   BwdParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -645,10 +655,14 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   p.n_chunk = a.n_chunk;
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
-  const int64_t rows = static_cast<int64_t>(a.n_blk) * kBlock * (a.hq / a.hkv);
-  const int64_t n_dq = (rows + 32 * kWaves - 1) / (32 * kWaves) * a.hkv;
-  dq_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_dq)), dim3(kT), 0, s>>>(p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  p.dq_overwrite = (a.flags & SXA_BWD_DQ_OVERWRITE) != 0;
+  if (a.flags & SXA_BWD_DQ) {
+    const int64_t rows = static_cast<int64_t>(a.n_blk) * kBlock * (a.hq / a.hkv);
+    const int64_t n_dq = (rows + 32 * kWaves - 1) / (32 * kWaves) * a.hkv;
+    dq_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_dq)), dim3(kT), 0, s>>>(p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (!(a.flags & SXA_BWD_DKDV)) return hipSuccess;
   const int64_t n_ctx_tiles = (a.n_loc + kKeysPerWG - 1) / kKeysPerWG;
   const int64_t n_self_tiles =
       a.k_self ? (static_cast<int64_t>(a.n_blk) * kBlock + kKeysPerWG - 1) / kKeysPerWG : 0;

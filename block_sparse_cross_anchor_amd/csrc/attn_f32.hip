@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const T* __restrict__ o
 
 // Query-major backward: dq_accum[i][h] += scale * sum_j dS_ij K_j over this call's keys.
 template <int D>
-__global__ __launch_bounds__(kThreads) void dq_f32_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) void dq_f32_kernel(AttnArgs a, bool overwrite) {
   constexpr int CPT = D / 16;
   const int b = blockIdx.x, h = blockIdx.y;
   const int g = h / (a.hq / a.hkv);
@@ -201,7 +201,10 @@ __global__ __launch_bounds__(kThreads) void dq_f32_kernel(AttnArgs a) {
   });
   const int64_t orow = static_cast<int64_t>(kBlock * b + row) * a.hq + h;
 #pragma unroll
-  for (int u = 0; u < CPT; ++u) a.dq[orow * D + cg + 16 * u] += a.scale * acc[u];
+  for (int u = 0; u < CPT; ++u) {
+    float* dst = a.dq + orow * D + cg + 16 * u;
+    *dst = overwrite ? a.scale * acc[u] : *dst + a.scale * acc[u];
+  }
 }
 
 // Key-major backward over tiles of 16 key rows: the local context rows, then (when
@@ -331,10 +334,15 @@ hipError_t launch_fwd_f32_d(const AttnArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_bwd_f32_d(const AttnArgs& a, hipStream_t s) {
-  hipError_t e = launch_delta(a, false, s);
-  if (e != hipSuccess) return e;
-  dq_f32_kernel<D><<<dim3(a.n_blk, a.hq), kThreads, 0, s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (a.flags & SXA_BWD_DELTA) {
+    if ((e = launch_delta(a, false, s)) != hipSuccess) return e;
+  }
+  if (a.flags & SXA_BWD_DQ) {
+    dq_f32_kernel<D><<<dim3(a.n_blk, a.hq), kThreads, 0, s>>>(a, (a.flags & SXA_BWD_DQ_OVERWRITE) != 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (!(a.flags & SXA_BWD_DKDV)) return hipSuccess;
   const int n_ctx_tiles = static_cast<int>((a.n_loc + kBlock - 1) / kBlock);
   const int n_tiles = n_ctx_tiles + (a.k_self != nullptr ? a.n_blk : 0);
   if (n_tiles == 0) return hipSuccess;

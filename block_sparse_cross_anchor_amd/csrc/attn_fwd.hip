@@ -220,6 +220,48 @@ fwd_bf16_kernel(FwdParams p) {
     HI = max(HI, p.anchor[b]);
   }
 
+  Walk w;
+  w.self_pos = p.k_self ? kBlock * b_first : 0;
+  w.self_end = p.k_self ? kBlock * (b_last + 1) : 0;
+  w.c = -1;
+  w.off = 0;
+  w.gs = w.len = w.t = w.t_end = 0;
+
+  float m[NT], l[NT];
+  f32x16 oacc[DT][NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = -INFINITY;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][nt][r] = 0.f;
+  }
+
+  Tile cur, nxt;
+  const bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
+  if (!have) {  // no allowed key in this call: O = 0, lse = -inf
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t r = wg_row0 + 32 * NT * wave + 32 * nt + l32;
+      if (r >= R) continue;
+      const int64_t tok = r / grp;
+      const int64_t orow = tok * p.hq + static_cast<int64_t>(g) * grp + static_cast<int>(r % grp);
+      if (h2 == 0) p.lse[orow] = -INFINITY;
+#pragma unroll
+      for (int d0 = h2 * (D / 2); d0 < (h2 + 1) * (D / 2); d0 += 8) {
+        if constexpr (OUT_BF16)
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.o) + orow * D + d0) = u32x4{0, 0, 0, 0};
+        else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + orow * D + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + orow * D + d0 + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+    return;
+  }
+
   // per-lane query columns (one per 32-row N tile)
   int clo[NT], chi[NT], slo[NT], shi[NT];
   int64_t orow[NT];
@@ -245,35 +287,12 @@ fwd_bf16_kernel(FwdParams p) {
     }
   }
 
-  Walk w;
-  w.self_pos = p.k_self ? kBlock * b_first : 0;
-  w.self_end = p.k_self ? kBlock * (b_last + 1) : 0;
-  w.c = -1;
-  w.off = 0;
-  w.gs = w.len = w.t = w.t_end = 0;
-
-  float m[NT], l[NT];
-  f32x16 oacc[DT][NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m[nt] = -INFINITY;
-    l[nt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][nt][r] = 0.f;
-  }
-
-  Tile cur, nxt;
   TileRegs<D, T> regs;
-  bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
-  if (have) {
-    regs.load(cur, p, g, tid);
-    regs.store(lds[0][0], lds[0][1], tid);
-    __syncthreads();
-  }
+  regs.load(cur, p, g, tid);
+  regs.store(lds[0][0], lds[0][1], tid);
+  __syncthreads();
   int buf = 0;
-  while (have) {
+  while (true) {
     const bool has_next = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, nxt);
     if (has_next) regs.load(nxt, p, g, tid);
 

@@ -38,6 +38,7 @@ struct AttnArgs {
   void* dv;
   void* dk_self;
   void* dv_self;
+  int32_t flags;  // SXA_BWD_* phases (never 0 here)
 };
 
 // Launchers: return hipSuccess or the launch error.
@@ -52,6 +53,9 @@ hipError_t launch_combine(const void* o_parts, bool part_bf16, const float* lse_
 // Zero n_words 32-bit words with a fill kernel (no hipMemsetAsync, so the call is
 // safe inside a captured graph).
 hipError_t launch_zero_words(void* p, int64_t n_words, hipStream_t s);
+hipError_t launch_context_gather(const void* src, int64_t row_bytes, const int32_t* chunk_gstart,
+                                 const int32_t* chunk_len, int32_t n_chunk, int64_t n_dst_rows,
+                                 void* dst, hipStream_t s);
 hipError_t launch_chunk_cost(const int32_t* anchor, const int32_t* sample_start, int32_t n_blk,
                              int32_t n_ctx, int32_t chunk_size, int64_t* cost, hipStream_t s);
 

@@ -19,10 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libsxattn.so")
 
 SXA_F32, SXA_BF16 = 0, 1
 SXA_OK, SXA_EINVAL, SXA_EUNSUPPORTED, SXA_EHIP = 0, -1, -2, -3
+BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_DQ_OVERWRITE = 1, 2, 4, 8
 BLOCK = 16
 
 EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_bwd", "lse_combine", "chunk_cost", "lpt_assign",
-           "sxa_last_error")
+           "context_gather", "sxa_last_error")
 
 _lib = None
 
@@ -46,7 +47,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     attn_common = [P, P, P, ctypes.c_int, I32, I32, I32, I32, I32, F32, P, P, P, P, I32, I64, P, P]
     lib.sparse_xattn_fwd.argtypes = attn_common + [P, ctypes.c_int, P, P]
     lib.sparse_xattn_fwd.restype = ctypes.c_int
-    lib.sparse_xattn_bwd.argtypes = attn_common + [P, P, P, P, P, P, P, P, P, P]
+    lib.sparse_xattn_bwd.argtypes = attn_common + [P, P, P, P, P, P, P, P, P, I32, P]
     lib.sparse_xattn_bwd.restype = ctypes.c_int
     lib.lse_combine.argtypes = [P, ctypes.c_int, P, I32, I64, I32, P, ctypes.c_int, P, P]
     lib.lse_combine.restype = ctypes.c_int
@@ -54,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.chunk_cost.restype = ctypes.c_int
     lib.lpt_assign.argtypes = [P, I32, I32, P, P]
     lib.lpt_assign.restype = ctypes.c_int
+    lib.context_gather.argtypes = [P, I64, P, P, I32, I64, P, P]
+    lib.context_gather.restype = ctypes.c_int
     lib.sxa_last_error.argtypes = []
     lib.sxa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -142,9 +145,10 @@ def sparse_xattn_fwd(q, k, v, meta: Meta, scale: float, k_self=None, v_self=None
 
 def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
                      k_self=None, v_self=None, delta_ws=None, dk=None, dv=None, dk_self=None,
-                     dv_self=None):
-    """Backward of the local chunks (+ own-block term).  Adds into dq_accum (float32);
-    returns (dk, dv, dk_self, dv_self)."""
+                     dv_self=None, flags: int = 0):
+    """Backward of the local chunks (+ own-block term).  Adds into dq_accum (float32)
+    unless BWD_DQ_OVERWRITE is set; ``flags`` selects phases (0 = all).
+    Returns (dk, dv, dk_self, dv_self)."""
     n_q, hq, d = q.shape
     hkv = k.shape[1]
     _need(q, "q")
@@ -173,7 +177,7 @@ def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
         _ptr(meta.anchor), _ptr(meta.sample_start), _ptr(meta.chunk_gstart), _ptr(meta.chunk_len),
         meta.n_chunk, meta.n_loc, _ptr(k_self), _ptr(v_self), _ptr(o), _ptr(dout), _ptr(lse),
         _ptr(delta_ws), _ptr(dq_accum), _ptr(dk), _ptr(dv), _ptr(dk_self), _ptr(dv_self),
-        _stream()))
+        int(flags), _stream()))
     return dk, dv, dk_self, dv_self
 
 
@@ -205,6 +209,22 @@ def chunk_cost(anchor, sample_start, n_ctx: int, chunk_size: int, out=None):
     lib = load_library()
     _check(lib.chunk_cost(_ptr(anchor), _ptr(sample_start), int(anchor.numel()), BLOCK, int(n_ctx),
                           int(chunk_size), _ptr(out), _stream()))
+    return out
+
+
+def context_gather(src, chunk_gstart, chunk_len, n_rows: int, out=None):
+    """Rows of the listed chunks of ``src`` ([rows, ...] device tensor) back to back.
+    chunk_gstart / chunk_len: int32 device tensors; n_rows = sum of the lengths."""
+    _need(src, "src")
+    _need(chunk_gstart, "chunk_gstart", dtype=torch.int32)
+    _need(chunk_len, "chunk_len", chunk_gstart.shape, torch.int32)
+    if out is None:
+        out = torch.empty((int(n_rows),) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    _need(out, "out", (int(n_rows),) + tuple(src.shape[1:]), src.dtype)
+    row_bytes = src[0].numel() * src.element_size() if src.shape[0] else 16
+    lib = load_library()
+    _check(lib.context_gather(_ptr(src), row_bytes, _ptr(chunk_gstart), _ptr(chunk_len),
+                              int(chunk_gstart.numel()), int(n_rows), _ptr(out), _stream()))
     return out
 
 

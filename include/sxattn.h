@@ -88,17 +88,29 @@ int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                      int64_t n_loc, const void* k_self, const void* v_self,
                      void* o, sxa_dtype o_dtype, float* lse, void* stream);
 
+/* Phases of sparse_xattn_bwd (bit flags; 0 means all of DELTA | DQ | DKDV). */
+enum {
+  SXA_BWD_DELTA = 1,         /* pre-pass: delta_ws = rowsum(dout * o) */
+  SXA_BWD_DQ = 2,            /* add this call's query gradient to dq_accum */
+  SXA_BWD_DKDV = 4,          /* write dk, dv (and dk_self, dv_self) */
+  SXA_BWD_DQ_OVERWRITE = 8   /* with SXA_BWD_DQ: overwrite dq_accum instead of adding */
+};
+
 /*
  * Backward of this call's chunks (and own-block term if k_self != NULL), from the
  * merged output o, merged lse and upstream gradient dout (all [n_q][hq], dtype
  * in_dtype for o/dout).  Keys/values stay local: the gradient of the local rows is
  * produced here ("Exchange the smaller side": local in forward and backward).
- *   delta_ws [n_q][hq] float32 scratch (overwritten with rowsum(dout * o)).
- *   dq_accum [n_q][hq][d] float32: this call's query gradient is ADDED to it, so
- *            per-chunk calls accumulate.
+ *   delta_ws [n_q][hq] float32: written by the SXA_BWD_DELTA phase, read by the
+ *            others (a caller that already holds rowsum(dout * o) from an earlier
+ *            call with the same o and dout may skip the phase).
+ *   dq_accum [n_q][hq][d] float32: this call's query gradient is ADDED to it (or
+ *            written, with SXA_BWD_DQ_OVERWRITE), so per-chunk calls accumulate.
  *   dk, dv   [n_loc][hkv][d] in in_dtype: overwritten.
  *   dk_self, dv_self [n_q][hkv][d] in in_dtype: overwritten when k_self != NULL
  *            (must then be non-NULL), ignored otherwise.
+ *   flags    SXA_BWD_* bits selecting the phases; they run in the order
+ *            DELTA, DQ, DKDV on `stream`.
  */
 int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_dtype,
                      int32_t n_blk, int32_t block_size, int32_t hq, int32_t hkv, int32_t d,
@@ -107,7 +119,7 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                      int64_t n_loc, const void* k_self, const void* v_self,
                      const void* o, const void* dout, const float* lse,
                      float* delta_ws, float* dq_accum, void* dk, void* dv,
-                     void* dk_self, void* dv_self, void* stream);
+                     void* dk_self, void* dv_self, int32_t flags, void* stream);
 
 /*
  * Exact merge of n_parts partials from their log-sum-exp statistics
@@ -147,6 +159,20 @@ int chunk_cost(const int32_t* anchor, const int32_t* sample_start, int32_t n_blk
  */
 int lpt_assign(const int64_t* cost, int32_t n_chunk, int32_t n_bin, int32_t* bin_of_chunk,
                int64_t* bin_load);
+
+/*
+ * Context redistribution: copy the rows of the listed chunks of a packed context
+ * tensor back to back into a device's local buffer ("Balance actual attention
+ * work": after planning, context chunks are moved once per step to the device
+ * that owns them).
+ *   src [n_src_rows][row_bytes] device; chunk i covers src rows
+ *   [chunk_gstart[i], chunk_gstart[i] + chunk_len[i]) (device int32 arrays);
+ *   dst [sum chunk_len][row_bytes] device, overwritten.  row_bytes must be a
+ *   multiple of 16; chunks must lie inside src (not validated on the device).
+ */
+int context_gather(const void* src, int64_t row_bytes, const int32_t* chunk_gstart,
+                   const int32_t* chunk_len, int32_t n_chunk, int64_t n_dst_rows, void* dst,
+                   void* stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* sxa_last_error(void);

@@ -191,3 +191,42 @@ def test_bwd_4k_queries_32k_context_per_chunk_sampled():
             continue
         assert rel_frob(host64(dk)[start:start + 64], rr[1]) <= 3e-2
         assert rel_frob(host64(dv)[start:start + 64], rr[2]) <= 3e-2
+
+
+def test_bwd_phase_flags_match_one_call():
+    """DELTA, DQ (overwrite), DKDV issued as separate calls give the same bits as
+    one call with all phases on a zeroed dq_accum."""
+    w = W["fwd_bf16_512q_4k"]
+    gs, gl = synth.contiguous_chunks(w.n_ctx, w.chunk_size)
+    meta = synth.meta_for(w, 12)
+    inp = synth.draw_inputs(12, meta, w.hq, w.hkv, w.d, "bf16", 1.0, gs, gl, with_dout=True)
+    scale = 1.0 / math.sqrt(w.d)
+    dm = device_meta(meta, gs, gl)
+    o, lse = gpu_fwd_merged(meta, inp, scale, dm)
+    q, k, v, do, ks, vs = (dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.dout), dev(inp.k_self),
+                           dev(inp.v_self))
+    dq1 = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+    r1 = sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o, do, lse, dq1, ks, vs)
+    dq2 = torch.full(q.shape, 7.0, dtype=torch.float32, device="cuda")  # overwritten
+    delta = torch.empty(lse.shape, dtype=torch.float32, device="cuda")
+    sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o, do, lse, dq2, ks, vs, delta_ws=delta,
+                            flags=sxattn.BWD_DELTA)
+    sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o, do, lse, dq2, ks, vs, delta_ws=delta,
+                            flags=sxattn.BWD_DQ | sxattn.BWD_DQ_OVERWRITE)
+    r2 = sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o, do, lse, dq2, ks, vs, delta_ws=delta,
+                                 flags=sxattn.BWD_DKDV)
+    torch.cuda.synchronize()
+    assert torch.equal(dq1, dq2)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    # overwrite on a call whose chunks reach no query row clears dq_accum
+    late = np.array([w.n_ctx - 1], np.int32), np.array([1], np.int32)
+    dm1 = device_meta(meta, *late)
+    dq3 = torch.full(q.shape, 7.0, dtype=torch.float32, device="cuda")
+    sxattn.sparse_xattn_bwd(q, k[-1:].contiguous(), v[-1:].contiguous(), dm1, scale, o, do, lse,
+                            dq3, delta_ws=delta, flags=sxattn.BWD_DQ | sxattn.BWD_DQ_OVERWRITE)
+    torch.cuda.synchronize()
+    want = oracle.sparse_xattn_bwd(inp.q.f64, inp.k.f64[-1:], inp.v.f64[-1:], host64(o),
+                                   inp.dout.f64, host64(lse), meta.anchor, meta.sample_start,
+                                   *late, scale)[0]
+    np.testing.assert_allclose(host64(dq3), want, atol=1e-6)

@@ -313,3 +313,23 @@ def test_fwd_headline_shape_sampled_rows():
                                      sub.sample_start, gs, gl, scale, inp.k_self.f64[rows],
                                      inp.v_self.f64[rows])
     check_bf16(o[torch.as_tensor(rows).cuda()], l[torch.as_tensor(rows).cuda()], ro, rl)
+
+
+# ----------------------------------------------------------------------------- redistribution
+
+@pytest.mark.parametrize("row_shape,dtype", [((8, 128), torch.bfloat16), ((2, 64), torch.float32),
+                                             ((1, 8), torch.bfloat16)])
+def test_context_gather_bit_exact(row_shape, dtype):
+    rng = np.random.default_rng(3)
+    n = 5000
+    src = torch.randn((n,) + row_shape, generator=torch.Generator().manual_seed(1)).to(dtype).cuda()
+    cuts = np.sort(rng.choice(np.arange(1, n), size=11, replace=False))
+    starts = np.concatenate([[0], cuts]).astype(np.int32)
+    lens = np.diff(np.concatenate([starts, [n]])).astype(np.int32)
+    pick = rng.permutation(len(starts))[:7]
+    gs, gl = starts[pick], lens[pick]
+    out = sxattn.context_gather(src, torch.as_tensor(gs).cuda(), torch.as_tensor(gl).cuda(),
+                                int(gl.sum()))
+    torch.cuda.synchronize()
+    want = src.cpu()[torch.as_tensor(synth.chunk_rows(gs, gl))]
+    assert torch.equal(out.cpu(), want)
