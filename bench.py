@@ -107,10 +107,10 @@ def build_problem(torch, seed):
     bf, f32 = torch.bfloat16, torch.float32
     P["k_loc"] = torch.empty((nb, n_loc, hkv, d), dtype=bf, device="cuda")
     P["v_loc"] = torch.empty_like(P["k_loc"])
-    P["dk_loc"] = torch.empty_like(P["k_loc"])
-    P["dv_loc"] = torch.empty_like(P["k_loc"])
-    P["dks"] = torch.empty_like(P["ks"])
-    P["dvs"] = torch.empty_like(P["vs"])
+    P["dk_loc"] = torch.empty((nb, n_loc, hkv, d), dtype=f32, device="cuda")
+    P["dv_loc"] = torch.empty_like(P["dk_loc"])
+    P["dks"] = torch.empty(P["ks"].shape, dtype=f32, device="cuda")
+    P["dvs"] = torch.empty_like(P["dks"])
     P["o_parts"] = torch.empty((nb, n_q, hq, d), dtype=bf, device="cuda")
     P["lse_parts"] = torch.empty((nb, n_q, hq), dtype=f32, device="cuda")
     P["o"] = torch.empty((n_q * hq, d), dtype=bf, device="cuda")

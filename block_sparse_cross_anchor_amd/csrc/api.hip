@@ -120,8 +120,8 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                      const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
                      int64_t n_loc, const void* k_self, const void* v_self, const void* o,
                      const void* dout, const float* lse, float* delta_ws, float* dq_accum,
-                     void* dk, void* dv, void* dk_self, void* dv_self, int32_t flags,
-                     void* stream) {
+                     void* dk, void* dv, void* dk_self, void* dv_self, void* workspace,
+                     int64_t workspace_bytes, int32_t flags, void* stream) {
   sxa::AttnArgs a;
   int st = check_attn(q, k, v, in_dtype, n_blk, block_size, hq, hkv, d, scale, anchor,
                       sample_start, chunk_gstart, chunk_len, n_chunk, n_loc, k_self, v_self, a);
@@ -147,18 +147,26 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
   a.dk_self = dk_self;
   a.dv_self = dv_self;
   a.flags = flags;
+  if (workspace_bytes < 0) return fail(SXA_EINVAL, "workspace_bytes must be >= 0");
+  const int64_t need = sxa::bwd_workspace_bytes(n_loc, hkv, d);
+  a.workspace = (workspace != nullptr && need > 0 && workspace_bytes >= need) ? workspace : nullptr;
+  a.workspace_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_blk == 0) {
     if (!(flags & SXA_BWD_DKDV)) return ok();
     // no query: the gradients of the local keys/values are zero
-    const int64_t es = in_dtype == SXA_BF16 ? 2 : 4;
-    const int64_t kv_words = n_loc * hkv * d * es / 4;
+    const int64_t kv_words = n_loc * hkv * d;  // float32 gradients
     hipError_t e = sxa::launch_zero_words(dk, kv_words, s);
     if (e == hipSuccess) e = sxa::launch_zero_words(dv, kv_words, s);
     return hip_status(e, "sparse_xattn_bwd zero fill");
   }
   return hip_status(in_dtype == SXA_BF16 ? sxa::launch_bwd_bf16(a, s) : sxa::launch_bwd_f32(a, s),
                     "sparse_xattn_bwd launch");
+}
+
+int64_t sparse_xattn_bwd_workspace_bytes(int64_t n_loc, int32_t hkv, int32_t d) {
+  if (n_loc < 0 || hkv <= 0 || (d != 64 && d != 128)) return 0;
+  return sxa::bwd_workspace_bytes(n_loc, hkv, d);
 }
 
 int lse_combine(const void* o_parts, sxa_dtype part_dtype, const float* lse_parts,

@@ -22,6 +22,7 @@
 // cross-workgroup reductions of dQ.
 #include "device_common.h"
 #include "internal.h"
+#include "lds_tile.h"
 
 namespace sxa {
 namespace {
@@ -40,10 +41,10 @@ struct BwdParams {
   const float* lse;
   const float* delta;
   float* dq;
-  uint16_t* dk;
-  uint16_t* dv;
-  uint16_t* dk_self;
-  uint16_t* dv_self;
+  float* dk;
+  float* dv;
+  float* dk_self;
+  float* dv_self;
   const int32_t* anchor;
   const int32_t* sample_start;
   const int32_t* chunk_gstart;
@@ -53,16 +54,11 @@ struct BwdParams {
   float scale;
   float scale_log2;  // scale * log2(e)
   int32_t dq_overwrite;
+  int32_t* ws_parts;  // dK/dV split scratch: parts per (context tile, kv head), or nullptr
+  float* ws_slots;    // [tile][hkv][kMaxParts][keys per tile][2][D] partial dK, dV
 };
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
-
-// position of index i inside a 16-aligned group when bits 2 and 3 are swapped:
-// the order in which one lane holds MFMA accumulator rows 8*(r/4) + 4h + r%4
-__device__ __forceinline__ int perm23(int i) {
-  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
-}
-__device__ __forceinline__ int swz64(int d) { return (d & 7) ^ ((d >> 3) & 7); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return static_cast<uint32_t>(f32_to_bf16_bits(a)) | (static_cast<uint32_t>(f32_to_bf16_bits(b)) << 16);
@@ -123,72 +119,38 @@ __device__ __forceinline__ bool walk_next(Walk& w, const int32_t* __restrict__ c
   }
 }
 
-// K tile: row-major (16-byte chunks XOR (key & 7)) and transposed (64 keys per
-// head-dim row, keys permuted by perm23, chunks XOR swz64(d)); V tile row-major.
+// K and V tiles staged row-major (lds_tile.h); K^T for dQ comes from the
+// transposing read of the same K tile.
 template <int D>
 struct DqTileRegs {
   static constexpr int CPR = D / 8;
-  static constexpr int KIT = kTileKeys / 2 * CPR;  // (key pair, chunk) items
-  static constexpr int VCH = kTileKeys * CPR;      // V chunks
-  static constexpr int KL = (KIT + kT - 1) / kT;
-  static constexpr int VL = (VCH + kT - 1) / kT;
-  u32x4 k[KL][2];
-  u32x4 v[VL];
+  static constexpr int CH = kTileKeys * CPR;
+  static constexpr int L = (CH + kT - 1) / kT;
+  u32x4 k[L], v[L];
 
   __device__ __forceinline__ void load(const Tile& t, const BwdParams& p, int g, int tid) {
     const uint16_t* K = t.self ? p.k_self : p.k;
     const uint16_t* V = t.self ? p.v_self : p.v;
     const int last = t.nrows - 1;
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int it = tid + kT * i;
-      if (KIT % kT == 0 || it < KIT) {
-        const int q2 = it / CPR, j = it % CPR;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int key = min(2 * q2 + kk, last);
-          k[i][kk] = *reinterpret_cast<const u32x4*>(K + ((t.row0 + key) * p.hkv + g) * D + 8 * j);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VL; ++i) {
+    for (int i = 0; i < L; ++i) {
       const int idx = tid + kT * i;
-      if (VCH % kT == 0 || idx < VCH) {
+      if (CH % kT == 0 || idx < CH) {
         const int key = min(idx / CPR, last), j = idx % CPR;
-        v[i] = *reinterpret_cast<const u32x4*>(V + ((t.row0 + key) * p.hkv + g) * D + 8 * j);
+        const int64_t off = ((t.row0 + key) * p.hkv + g) * D + 8 * j;
+        k[i] = *reinterpret_cast<const u32x4*>(K + off);
+        v[i] = *reinterpret_cast<const u32x4*>(V + off);
       }
     }
   }
 
-  __device__ __forceinline__ void store(uint16_t* lk, uint16_t* lkt, uint16_t* lv, int tid) const {
+  __device__ __forceinline__ void store(uint16_t* lk, uint16_t* lv, int tid) const {
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int it = tid + kT * i;
-      if (KIT % kT == 0 || it < KIT) {
-        const int q2 = it / CPR, j = it % CPR;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int key = 2 * q2 + kk;
-          *reinterpret_cast<u32x4*>(lk + key * D + 8 * (j ^ (key & 7))) = k[i][kk];
-        }
-        const int pos = perm23(2 * q2);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 8 * j + e;
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const uint32_t w = __builtin_amdgcn_perm(k[i][1][e >> 1], k[i][0][e >> 1], sel);
-          const int phys = (pos >> 3) ^ swz64(d);
-          *reinterpret_cast<uint32_t*>(lkt + d * kTileKeys + 8 * phys + (pos & 7)) = w;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VL; ++i) {
+    for (int i = 0; i < L; ++i) {
       const int idx = tid + kT * i;
-      if (VCH % kT == 0 || idx < VCH) {
-        const int key = idx / CPR, j = idx % CPR;
-        *reinterpret_cast<u32x4*>(lv + key * D + 8 * (j ^ (key & 7))) = v[i];
+      if (CH % kT == 0 || idx < CH) {
+        LdsTile<D>::store(lk, idx / CPR, idx % CPR, k[i]);
+        LdsTile<D>::store(lv, idx / CPR, idx % CPR, v[i]);
       }
     }
   }
@@ -199,7 +161,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int ROWS = 32 * kWaves;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][3][kTileKeys * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileKeys * D];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
@@ -264,7 +226,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
 
   DqTileRegs<D> regs;
   regs.load(cur, p, g, tid);
-  regs.store(lds[0][0], lds[0][1], lds[0][2], tid);
+  regs.store(lds[0][0], lds[0][1], tid);
   __syncthreads();
   int buf = 0;
   while (have) {
@@ -278,8 +240,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
     if (__any(any)) {
       const bool all_full = __all(full);
       const uint16_t* lk = lds[buf][0];
-      const uint16_t* lkt = lds[buf][1];
-      const uint16_t* lv = lds[buf][2];
+      const uint16_t* lv = lds[buf][1];
       f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -289,10 +250,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const int key = 32 * mt + l32;
-          const int off = key * D + 8 * ((2 * ks + h2) ^ (key & 7));
-          const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lk + off));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lv + off));
+          const bf16x8 kf = LdsTile<D>::frag(lk, 32 * mt + l32, 2 * ks + h2);
+          const bf16x8 vf = LdsTile<D>::frag(lv, 32 * mt + l32, 2 * ks + h2);
           sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
           pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[ks], pacc[mt], 0, 0, 0);
         }
@@ -314,15 +273,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
       for (int kq = 0; kq < 4; ++kq) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int d = 32 * dt + l32;
-          const bf16x8 kt = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(lkt + d * kTileKeys + 8 * ((2 * kq + h2) ^ swz64(d))));
+          const int sl = lane & 15;
+          const bf16x8 kt = LdsTile<D>::frag_t(lk, tr_row_a(kq, h2, sl), tr_row_b(kq, h2, sl),
+                                               32 * dt + 16 * ((lane >> 4) & 1), sl);
           dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[kq], dqacc[dt], 0, 0, 0);
         }
       }
     }
 
-    if (has_next) regs.store(lds[buf ^ 1][0], lds[buf ^ 1][1], lds[buf ^ 1][2], tid);
+    if (has_next) regs.store(lds[buf ^ 1][0], lds[buf ^ 1][1], tid);
     __syncthreads();
     if (!has_next) break;
     cur = nxt;
@@ -345,38 +304,51 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
 // ============================================================================ dkdv kernel
 //
 // Workgroup: 8 waves x 32 keys = 256 consecutive key rows of one kv head (local
-// context rows, or own-block rows for the tiles after the context ones).  Query
-// rows of kv head g are numbered r = token * grp + (h - g*grp) and visited in
-// steps of 32.  A step is visited when one of its blocks' key intervals meets
-// the workgroup's keys (for own-block tiles: when it holds one of their blocks).
+// context rows, or own-block rows for the tiles after the context ones).  K of a
+// wave's keys is held in registers (MFMA B operand of S = Q K^T); V of the
+// workgroup's keys sits in LDS (B operand of dP = dO V^T).  Query rows of kv head
+// g are numbered r = token * grp + (h - g*grp) and visited in steps of 32 rows;
+// a step is visited when one of its blocks' key intervals meets the workgroup's
+// keys (own-block tiles: when it holds one of their blocks).  When the group size
+// is even a step lies inside one block, so its mask is one interval ("uniform").
 
 constexpr int kKeysPerWG = 32 * kWaves;
 constexpr int kStepRows = 32;
+constexpr int kStepsPerPart = 112;  // query steps per workgroup above which a tile is split
+constexpr int kMaxParts = 4;
 
-struct StepLds {
-  int lo[kStepRows];   // per row: allowed key interval [lo, hi) in key coordinates
+struct StepMeta {
+  float lse2[kStepRows];  // log2-domain lse per row (+inf: row contributes nothing)
+  float dlt[kStepRows];   // delta per row
+  int lo[kStepRows];      // per-row allowed key interval (non-uniform steps)
   int hi[kStepRows];
-  float lse2[kStepRows];
-  float dlt[kStepRows];
+  int uni, lo0, hi0;      // uniform step: one interval for all rows
 };
 
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dkdv_bf16_kernel(BwdParams p,
-                                                                                      int n_ctx_tiles) {
+                                                                                      int n_ctx_tiles,
+                                                                                      int n_tiles) {
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int CPR = D / 8;
-  // per stage: Q row-major, Q^T, dO row-major, dO^T (32 rows each)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][4][kStepRows * D];
-  __shared__ StepLds meta[2];
+  constexpr int SCH = 2 * kStepRows * CPR;  // 16-byte chunks of Q and dO rows of one step
+  constexpr int SL = (SCH + kT - 1) / kT;
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[kKeysPerWG * D];
+  // per stage: Q and dO rows of the step, row-major (transposed operands via tr reads)
+  __shared__ __attribute__((aligned(16))) uint16_t stg[2][2][kStepRows * D];
+  __shared__ __attribute__((aligned(16))) StepMeta meta[2];
   __shared__ int step_list[kT];
   __shared__ int wave_cnt[kWaves];
   __shared__ int red[2][kWaves];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
-  const int g = blockIdx.x % p.hkv;
-  const int tile = blockIdx.x / p.hkv;
+  // blockIdx -> (part, tile, kv head); all first parts are dispatched first
+  const int per_part = n_tiles * p.hkv;
+  const int part = blockIdx.x / per_part;
+  const int g = (blockIdx.x % per_part) % p.hkv;
+  const int tile = (blockIdx.x % per_part) / p.hkv;
   const bool self_tile = tile >= n_ctx_tiles;
   const int grp = p.hq / p.hkv;
   const int64_t n_q = static_cast<int64_t>(p.n_blk) * kBlock;
@@ -388,15 +360,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dkdv_bf16_k
   const uint16_t* V = self_tile ? p.v_self : p.v;
 
   // this lane's key (column of the S tile): local row and key coordinate
-  const int64_t kr = krow0 + 32 * wave + l32;
+  const int krow = 32 * wave + l32;
+  const int64_t kr = krow0 + krow;
   const bool kvalid = kr < key_rows;
   const int64_t krc = kvalid ? kr : key_rows - 1;
-  int kcoord;  // global position (context) or own-block row (self)
+  int kcoord = 0;  // global position (context) or own-block row (self)
   if (self_tile) {
     kcoord = static_cast<int>(krc);
   } else {
     int64_t off = 0;
-    kcoord = 0;
     for (int c = 0; c < p.n_chunk; ++c) {
       const int len = p.chunk_len[c];
       if (krc < off + len) {
@@ -406,19 +378,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dkdv_bf16_k
       off += len;
     }
   }
-  const int kc_min_lane = kvalid ? kcoord : 0x7fffffff;
-  const int kc_max_lane = kvalid ? kcoord : -0x7fffffff;
-
-  // K and V of this lane's key as MFMA B operands (8 head-dim values per k-step)
-  bf16x8 kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(K + (krc * p.hkv + g) * D + 16 * ks + 8 * h2));
-    vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(V + (krc * p.hkv + g) * D + 16 * ks + 8 * h2));
-  }
-
   // key-coordinate range of the workgroup
-  int kmin = kc_min_lane, kmax = kc_max_lane;
+  int kmin = kvalid ? kcoord : 0x7fffffff, kmax = kvalid ? kcoord : -0x7fffffff;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     kmin = min(kmin, __shfl_xor(kmin, off, 64));
@@ -443,68 +404,71 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dkdv_bf16_k
 #pragma unroll
     for (int i = 0; i < 16; ++i) dkacc[dt][i] = dvacc[dt][i] = 0.f;
 
-  // step staging: thread -> (row pair, chunk) of Q (first half of threads) or dO
-  constexpr int ITEMS = kStepRows / 2 * CPR;  // per tensor
-  static_assert(2 * ITEMS <= kT, "one item per thread");
-  const bool is_do = tid >= ITEMS;
-  const int item = is_do ? tid - ITEMS : tid;
-  const bool has_item = tid < 2 * ITEMS;
-  const int ipair = item / CPR, ichunk = item % CPR;
+  // staging: chunk idx = tid + kT * i of [tensor (Q, dO)][row][chunk]
+  u32x4 sreg[SL];
 
-  auto step_row = [&](int64_t step, int i) -> int64_t { return step * kStepRows + i; };
-  auto row_gaddr = [&](int64_t row) -> int64_t {  // element offset of query row `row`
+  auto row_off = [&](int64_t row) -> int64_t {  // element offset of query row `row`
     const int64_t tk = row / grp;
     return (tk * p.hq + static_cast<int64_t>(g) * grp + row % grp) * D;
   };
-
-  u32x4 sreg[2];
+  // metadata of the staged step, prefetched with the rows: threads < 32 hold their
+  // row's lse / delta / interval, thread 32 the step's first block interval
+  float m_lse = 0.f, m_dlt = 0.f;
+  int m_lo = 0, m_hi = 0, m_uni = 0;
   auto load_step = [&](int64_t step) {
-    if (has_item) {
-      const uint16_t* src = is_do ? p.dout : p.q;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int64_t row = min(step_row(step, 2 * ipair + kk), R - 1);
-        sreg[kk] = *reinterpret_cast<const u32x4*>(src + row_gaddr(row) + 8 * ichunk);
-      }
-    }
-  };
-  auto store_step = [&](int64_t step, int b) {
-    if (has_item) {
-      uint16_t* rm = lds[b][is_do ? 2 : 0];
-      uint16_t* tr = lds[b][is_do ? 3 : 1];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int row = 2 * ipair + kk;
-        *reinterpret_cast<u32x4*>(rm + row * D + 8 * (ichunk ^ (row & 7))) = sreg[kk];
-      }
-      const int pos = perm23(2 * ipair);  // 32 rows: bit 4 kept
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * ichunk + e;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t w = __builtin_amdgcn_perm(sreg[1][e >> 1], sreg[0][e >> 1], sel);
-        const int phys = (pos >> 3) ^ ((d >> 1) & 3);
-        *reinterpret_cast<uint32_t*>(tr + d * kStepRows + 8 * phys + (pos & 7)) = w;
+    for (int i = 0; i < SL; ++i) {
+      const int idx = tid + kT * i;
+      if (SCH % kT == 0 || idx < SCH) {
+        const int tensor = idx / (kStepRows * CPR), rem = idx % (kStepRows * CPR);
+        const int64_t row = min(step * kStepRows + rem / CPR, R - 1);
+        sreg[i] = *reinterpret_cast<const u32x4*>((tensor == 0 ? p.q : p.dout) + row_off(row) + 8 * (rem % CPR));
       }
     }
     if (tid < kStepRows) {
-      const int64_t row_raw = step_row(step, tid);
+      const int64_t row_raw = step * kStepRows + tid;
       const bool rv = row_raw < R;
       const int64_t row = rv ? row_raw : R - 1;
       const int64_t tk = row / grp;
       const int bb = static_cast<int>(tk / kBlock);
       const int64_t li = tk * p.hq + static_cast<int64_t>(g) * grp + row % grp;
       const float ln = p.lse[li];
-      meta[b].lse2[tid] = (rv && ln != -INFINITY) ? ln * kLog2e : INFINITY;
-      meta[b].dlt[tid] = p.delta[li];
-      meta[b].lo[tid] = self_tile ? kBlock * bb : p.sample_start[bb];
-      meta[b].hi[tid] = rv ? (self_tile ? kBlock * bb + kBlock : p.anchor[bb]) : -0x7fffffff;
+      m_lse = (rv && ln != -INFINITY) ? ln * kLog2e : INFINITY;
+      m_dlt = p.delta[li];
+      m_lo = self_tile ? kBlock * bb : p.sample_start[bb];
+      m_hi = rv ? (self_tile ? kBlock * bb + kBlock : p.anchor[bb]) : -0x7fffffff;
+    } else if (tid == kStepRows) {
+      const int64_t r0 = step * kStepRows, r1 = r0 + kStepRows - 1;
+      const int b0 = static_cast<int>(r0 / grp / kBlock);
+      m_uni = r1 < R && static_cast<int>(r1 / grp / kBlock) == b0;
+      m_lo = self_tile ? kBlock * b0 : p.sample_start[b0];
+      m_hi = self_tile ? kBlock * b0 + kBlock : p.anchor[b0];
+    }
+  };
+  auto store_step = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      const int idx = tid + kT * i;
+      if (SCH % kT == 0 || idx < SCH) {
+        const int tensor = idx / (kStepRows * CPR), rem = idx % (kStepRows * CPR);
+        LdsTile<D>::store(stg[b][tensor], rem / CPR, rem % CPR, sreg[i]);
+      }
+    }
+    if (tid < kStepRows) {
+      meta[b].lse2[tid] = m_lse;
+      meta[b].dlt[tid] = m_dlt;
+      meta[b].lo[tid] = m_lo;
+      meta[b].hi[tid] = m_hi;
+    } else if (tid == kStepRows) {
+      meta[b].uni = m_uni;
+      meta[b].lo0 = m_lo;
+      meta[b].hi0 = m_hi;
     }
   };
 
-  // does a step hold a row whose block can read a key of this workgroup?
-  auto step_hits = [&](int64_t step) -> bool {
-    const int64_t r0 = step * kStepRows;
+  auto step_hit = [&](int64_t st) -> bool {
+    if (st >= n_steps) return false;
+    const int64_t r0 = st * kStepRows;
     const int64_t r1 = min(r0 + kStepRows, R) - 1;
     const int b0 = static_cast<int>(r0 / grp / kBlock), b1 = static_cast<int>(r1 / grp / kBlock);
     bool hit = false;
@@ -516,112 +480,170 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dkdv_bf16_k
     return hit;
   };
 
-  int buf = 0;
-  bool primed = false;
+  // Count the steps that reach this tile and split them over `parts` workgroups
+  // (interleaved), so that heavily read key tiles do not set the kernel's length.
+  int n_hit = 0;
+  for (int64_t base = 0; base < n_steps; base += kT) n_hit += __syncthreads_count(step_hit(base + tid));
+  const bool can_split = p.ws_parts != nullptr && !self_tile;
+  const int parts = can_split ? max(1, min(kMaxParts, (n_hit + kStepsPerPart - 1) / kStepsPerPart)) : 1;
+  if (part >= parts) return;
+  if (can_split && part == 0 && tid == 0) p.ws_parts[tile * p.hkv + g] = parts;
+
+  // V rows of the workgroup's keys -> LDS (row-major, chunk ^ (row & 7))
+  for (int idx = tid; idx < kKeysPerWG * CPR; idx += kT) {
+    const int row = idx / CPR, j = idx % CPR;
+    const int64_t src_row = min(krow0 + row, key_rows - 1);
+    LdsTile<D>::store(vtile, row, j, *reinterpret_cast<const u32x4*>(V + (src_row * p.hkv + g) * D + 8 * j));
+  }
+  bf16x8 kf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(K + (krc * p.hkv + g) * D + 16 * ks + 8 * h2));
+
+  int seen = 0;  // hits in earlier batches
   for (int64_t base = 0; base < n_steps; base += kT) {
-    // compact the steps of this batch that can touch the workgroup's keys
-    const int64_t st = base + tid;
-    const bool hit = st < n_steps && step_hits(st);
+    // compact this part's share of the batch's hits (global hit index % parts == part)
+    const bool hit = step_hit(base + tid);
     const uint64_t mask = __ballot(hit);
     if (lane == 0) wave_cnt[wave] = __popcll(mask);
     __syncthreads();
-    int pre = 0, total = 0;
+    int pre = 0, total_b = 0;
 #pragma unroll
     for (int w2 = 0; w2 < kWaves; ++w2) {
       const int c = wave_cnt[w2];
       pre += w2 < wave ? c : 0;
-      total += c;
+      total_b += c;
     }
-    if (hit) step_list[pre + __popcll(mask & ((uint64_t{1} << lane) - 1))] = static_cast<int>(st);
+    const int gidx = seen + pre + __popcll(mask & ((uint64_t{1} << lane) - 1));
+    // entries of this part: gidx = part + parts * j  ->  list slot j - first_j
+    const int first_j = (seen - part + parts - 1) / parts;  // first j with part + parts*j >= seen
+    if (hit && (gidx - part) % parts == 0) step_list[(gidx - part) / parts - first_j] = static_cast<int>(base + tid);
+    const int last_excl = seen + total_b;  // hits [seen, last_excl) are in this batch
+    const int end_j = (last_excl - part + parts - 1) / parts;
+    const int total = max(0, end_j - first_j);
+    seen = last_excl;
     __syncthreads();
     if (total == 0) continue;
 
-    if (!primed) {
-      load_step(step_list[0]);
-      store_step(step_list[0], 0);
-      __syncthreads();
-      primed = true;
-      buf = 0;
-    }
+    load_step(step_list[0]);
+    store_step(0);
+    __syncthreads();
+    int buf = 0;
     for (int si = 0; si < total; ++si) {
       const bool has_next = si + 1 < total;
       if (has_next) load_step(step_list[si + 1]);
 
-      // ---- this wave: 32 rows x 32 keys
-      const StepLds& mt = meta[buf];
-      // per-register rows 8*(i/4) + 4*h2 + i%4 of the step
-      bool allowed[16];
-      bool any = false, all = true;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i / 4) + 4 * h2 + (i % 4);
-        allowed[i] = kvalid && kcoord >= mt.lo[row] && kcoord < mt.hi[row];
-        any |= allowed[i];
-        all &= allowed[i];
+      const StepMeta& mt = meta[buf];
+      // wave-uniform step facts in scalar registers
+      const bool uni = __builtin_amdgcn_readfirstlane(mt.uni) != 0;
+      const int lo0 = __builtin_amdgcn_readfirstlane(mt.lo0);
+      const int hi0 = __builtin_amdgcn_readfirstlane(mt.hi0);
+      const bool lane_ok = kvalid && kcoord >= lo0 && kcoord < hi0;
+      bool run = true, all_ok = false;
+      if (uni) {
+        run = __any(lane_ok);
+        all_ok = __all(lane_ok);
       }
-      if (__any(any)) {
-        const bool all_ok = __all(all);
-        const uint16_t* lq = lds[buf][0];
-        const uint16_t* lqt = lds[buf][1];
-        const uint16_t* ld = lds[buf][2];
-        const uint16_t* ldt = lds[buf][3];
+      if (run) {
+        const uint16_t* lq = stg[buf][0];
+        const uint16_t* ld = stg[buf][1];
         f32x16 sacc, pacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int off = l32 * D + 8 * ((2 * ks + h2) ^ (l32 & 7));
-          const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lq + off));
-          const bf16x8 da = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ld + off));
+          const bf16x8 qa = LdsTile<D>::frag(lq, l32, 2 * ks + h2);
+          const bf16x8 da = LdsTile<D>::frag(ld, l32, 2 * ks + h2);
+          const bf16x8 vb = LdsTile<D>::frag(vtile, krow, 2 * ks + h2);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], pacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, pacc, 0, 0, 0);
         }
         bf16x8 pb[2], sb[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = 8 * (i / 4) + 4 * h2 + (i % 4);
-          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[i], p.scale_log2, -mt.lse2[row]));
-          if (!all_ok && !allowed[i]) pr = 0.f;
-          const float ds = pr * (pacc[i] - mt.dlt[row]);
-          pb[i / 8][i % 8] = static_cast<__bf16>(pr);
-          sb[i / 8][i % 8] = static_cast<__bf16>(ds);
+        for (int j = 0; j < 4; ++j) {
+          // rows 8j + 4h2 + 0..3 of the step
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&mt.lse2[8 * j + 4 * h2]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&mt.dlt[8 * j + 4 * h2]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -l4[i]));
+            if (!all_ok) {
+              if (uni) {
+                pr = lane_ok ? pr : 0.f;
+              } else {
+                const int row = 8 * j + 4 * h2 + i;
+                if (!(kvalid && kcoord >= mt.lo[row] && kcoord < mt.hi[row])) pr = 0.f;
+              }
+            }
+            const float ds = pr * (pacc[r] - d4[i]);
+            pb[r / 8][r % 8] = static_cast<__bf16>(pr);
+            sb[r / 8][r % 8] = static_cast<__bf16>(ds);
+          }
         }
 #pragma unroll
         for (int kq = 0; kq < 2; ++kq) {
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const int d = 32 * dt + l32;
-            const int off = d * kStepRows + 8 * ((2 * kq + h2) ^ ((d >> 1) & 3));
-            const bf16x8 dta = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ldt + off));
-            const bf16x8 qta = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lqt + off));
+            const int sl = lane & 15, col = 32 * dt + 16 * ((lane >> 4) & 1);
+            const bf16x8 dta = LdsTile<D>::frag_t(ld, tr_row_a(kq, h2, sl), tr_row_b(kq, h2, sl), col, sl);
+            const bf16x8 qta = LdsTile<D>::frag_t(lq, tr_row_a(kq, h2, sl), tr_row_b(kq, h2, sl), col, sl);
             dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dta, pb[kq], dvacc[dt], 0, 0, 0);
             dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, sb[kq], dkacc[dt], 0, 0, 0);
           }
         }
       }
 
-      if (has_next) store_step(step_list[si + 1], buf ^ 1);
+      if (has_next) store_step(buf ^ 1);
       __syncthreads();
-      if (has_next) buf ^= 1;
+      buf ^= 1;
     }
-    // the next batch restages from its first step
-    primed = false;
   }
 
   if (!kvalid) return;
-  uint16_t* dK = self_tile ? p.dk_self : p.dk;
-  uint16_t* dV = self_tile ? p.dv_self : p.dv;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int64_t o = (kr * p.hkv + g) * D + 32 * dt + 8 * jj + 4 * h2;
-      *reinterpret_cast<u32x2*>(dK + o) =
-          u32x2{pack_bf16x2(p.scale * dkacc[dt][4 * jj], p.scale * dkacc[dt][4 * jj + 1]),
-                pack_bf16x2(p.scale * dkacc[dt][4 * jj + 2], p.scale * dkacc[dt][4 * jj + 3])};
-      *reinterpret_cast<u32x2*>(dV + o) = u32x2{pack_bf16x2(dvacc[dt][4 * jj], dvacc[dt][4 * jj + 1]),
-                                                pack_bf16x2(dvacc[dt][4 * jj + 2], dvacc[dt][4 * jj + 3])};
+      const int dcol = 32 * dt + 8 * jj + 4 * h2;
+      const f32x4 kv4 = f32x4{dkacc[dt][4 * jj], dkacc[dt][4 * jj + 1], dkacc[dt][4 * jj + 2], dkacc[dt][4 * jj + 3]};
+      const f32x4 vv4 = f32x4{dvacc[dt][4 * jj], dvacc[dt][4 * jj + 1], dvacc[dt][4 * jj + 2], dvacc[dt][4 * jj + 3]};
+      if (parts == 1) {
+        float* dK = self_tile ? p.dk_self : p.dk;
+        float* dV = self_tile ? p.dv_self : p.dv;
+        const int64_t o = (kr * p.hkv + g) * D + dcol;
+        *reinterpret_cast<f32x4*>(dK + o) = kv4 * p.scale;
+        *reinterpret_cast<f32x4*>(dV + o) = vv4;
+      } else {  // partial sums of this part: added up by the reduce pass
+        float* slot = p.ws_slots + ((static_cast<int64_t>(tile) * p.hkv + g) * kMaxParts + part) *
+                                       (static_cast<int64_t>(kKeysPerWG) * 2 * D);
+        *reinterpret_cast<f32x4*>(slot + (krow * 2 + 0) * D + dcol) = kv4;
+        *reinterpret_cast<f32x4*>(slot + (krow * 2 + 1) * D + dcol) = vv4;
+      }
     }
+}
+
+// Sum of the partial dK/dV of split context tiles (one workgroup per tile and kv head).
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p) {
+  const int g = blockIdx.x % p.hkv;
+  const int tile = blockIdx.x / p.hkv;
+  const int parts = p.ws_parts[tile * p.hkv + g];
+  if (parts <= 1) return;
+  const int64_t slot_elems = static_cast<int64_t>(kKeysPerWG) * 2 * D;
+  const float* slots = p.ws_slots + (static_cast<int64_t>(tile) * p.hkv + g) * kMaxParts * slot_elems;
+  const int64_t krow0 = static_cast<int64_t>(tile) * kKeysPerWG;
+  constexpr int V4 = kKeysPerWG * 2 * D / 4;
+  for (int i = threadIdx.x; i < V4; i += 256) {
+    const int e = 4 * i;
+    const int krow = e / (2 * D), which = (e / D) % 2, dcol = e % D;
+    const int64_t kr = krow0 + krow;
+    if (kr >= p.n_loc) continue;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(slots + e);
+    for (int q = 1; q < parts; ++q) acc += *reinterpret_cast<const f32x4*>(slots + q * slot_elems + e);
+    float* dst = (which == 0 ? p.dk : p.dv) + (kr * p.hkv + g) * D + dcol;
+    *reinterpret_cast<f32x4*>(dst) = which == 0 ? acc * p.scale : acc;
+  }
 }
 
 template <int D>
@@ -640,10 +662,10 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   p.lse = a.lse_in;
   p.delta = a.delta;
   p.dq = a.dq;
-  p.dk = static_cast<uint16_t*>(a.dk);
-  p.dv = static_cast<uint16_t*>(a.dv);
-  p.dk_self = static_cast<uint16_t*>(a.dk_self);
-  p.dv_self = static_cast<uint16_t*>(a.dv_self);
+  p.dk = static_cast<float*>(a.dk);
+  p.dv = static_cast<float*>(a.dv);
+  p.dk_self = static_cast<float*>(a.dk_self);
+  p.dv_self = static_cast<float*>(a.dv_self);
   p.anchor = a.anchor;
   p.sample_start = a.sample_start;
   p.chunk_gstart = a.chunk_gstart;
@@ -656,6 +678,8 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   p.dq_overwrite = (a.flags & SXA_BWD_DQ_OVERWRITE) != 0;
+  p.ws_parts = nullptr;
+  p.ws_slots = nullptr;
   if (a.flags & SXA_BWD_DQ) {
     const int64_t rows = static_cast<int64_t>(a.n_blk) * kBlock * (a.hq / a.hkv);
     const int64_t n_dq = (rows + 32 * kWaves - 1) / (32 * kWaves) * a.hkv;
@@ -664,15 +688,34 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   }
   if (!(a.flags & SXA_BWD_DKDV)) return hipSuccess;
   const int64_t n_ctx_tiles = (a.n_loc + kKeysPerWG - 1) / kKeysPerWG;
-  const int64_t n_self_tiles =
-      a.k_self ? (static_cast<int64_t>(a.n_blk) * kBlock + kKeysPerWG - 1) / kKeysPerWG : 0;
-  const int64_t n_kv = (n_ctx_tiles + n_self_tiles) * a.hkv;
-  if (n_kv == 0) return hipSuccess;
-  dkdv_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_kv)), dim3(kT), 0, s>>>(p, static_cast<int>(n_ctx_tiles));
-  return hipGetLastError();
+  const int64_t n_q = static_cast<int64_t>(a.n_blk) * kBlock;
+  const int64_t n_self_tiles = a.k_self ? (n_q + kKeysPerWG - 1) / kKeysPerWG : 0;
+  const int64_t n_tiles = n_ctx_tiles + n_self_tiles;
+  if (n_tiles == 0) return hipSuccess;
+  const bool split = a.workspace != nullptr;
+  if (split) {
+    p.ws_parts = static_cast<int32_t*>(a.workspace);
+    p.ws_slots = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
+                                          ((n_ctx_tiles * a.hkv * 4 + 255) / 256) * 256);
+  }
+  const int64_t n_kv = n_tiles * a.hkv * (split ? kMaxParts : 1);
+  dkdv_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_kv)), dim3(kT), 0, s>>>(p, static_cast<int>(n_ctx_tiles),
+                                                                            static_cast<int>(n_tiles));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (split && n_ctx_tiles > 0) {
+    dkdv_reduce_kernel<D><<<dim3(static_cast<unsigned>(n_ctx_tiles * a.hkv)), dim3(256), 0, s>>>(p);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace
+
+int64_t bwd_workspace_bytes(int64_t n_loc, int32_t hkv, int32_t d) {
+  const int64_t tiles = (n_loc + kKeysPerWG - 1) / kKeysPerWG;
+  return ((tiles * hkv * 4 + 255) / 256) * 256 +
+         tiles * hkv * kMaxParts * static_cast<int64_t>(kKeysPerWG) * 2 * d * 4;
+}
 
 hipError_t launch_bwd_bf16(const AttnArgs& a, hipStream_t s) {
   return a.d == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);

@@ -28,16 +28,16 @@
 //                 result lane l holds column (query row) l % 32 and keys
 //                 8*(r/4) + 4h + r%4 of the 32-key M tile.
 //   O^T += V^T P^T with P^T taken straight from the S^T registers (converted to
-//                 bf16); the A operand is V^T, stored transposed in LDS with the
-//                 keys of each 16-key step permuted (bits 2 and 3 swapped) so that
-//                 the 8 keys a lane needs are one 16-byte read.
+//                 bf16); the A operand V^T is read from the row-major V tile with
+//                 the transposing LDS read (two ds_read_b64_tr_b16 per fragment),
+//                 in the key order the S^T registers hold.
 //   Row max needs one exchange between the two lane halves; row sums are kept
 //   per half and added once at the end.
-//   Both LDS tiles are XOR-swizzled in 16-byte units so that the 8-lane groups of
-//   ds_read_b128 hit distinct banks.
+//   Both LDS tiles are row-major, XOR-swizzled in 16-byte units (lds_tile.h).
 // Online softmax in base 2: x = s * scale * log2(e); p = exp2(x - m).
 #include "device_common.h"
 #include "internal.h"
+#include "lds_tile.h"
 
 namespace sxa {
 namespace {
@@ -117,26 +117,14 @@ __device__ __forceinline__ bool walk_next(Walk& w, const int32_t* __restrict__ c
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
-// key position inside a 64-key V^T row: bits 2 and 3 of the key index swapped
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
-__device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
-
 // Staging of one 64-key tile (K and V rows of one kv head) through registers into
-// LDS, split over all T threads of the workgroup.  K is stored row-major with the
-// 16-byte chunk index XOR-ed by (key & 7); V is stored transposed (one 64-key row
-// per head-dim element) with the key order permuted by vt_pos and the 16-byte
-// chunks XOR-ed by vt_swz(d).
+// row-major LDS tiles, split over all T threads of the workgroup.
 template <int D, int T>
 struct TileRegs {
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int KCH = kTileKeys * CPR;     // K chunks per tile
-  static constexpr int VIT = kTileKeys / 2 * CPR; // V items: (key pair, chunk)
-  static constexpr int KL = (KCH + T - 1) / T;
-  static constexpr int VL = (VIT + T - 1) / T;
-  u32x4 k[KL];
-  u32x4 v[VL][2];
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int CH = kTileKeys * CPR;   // chunks per tensor
+  static constexpr int L = (CH + T - 1) / T;
+  u32x4 k[L], v[L];
 
   // Rows past the tile end are clamped to its last row: those keys are masked, so
   // any finite value will do and the loads stay branch-free.
@@ -145,50 +133,24 @@ struct TileRegs {
     const uint16_t* V = t.self ? p.v_self : p.v;
     const int last = t.nrows - 1;
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
+    for (int i = 0; i < L; ++i) {
       const int idx = tid + T * i;
-      if (KCH % T == 0 || idx < KCH) {
+      if (CH % T == 0 || idx < CH) {
         const int key = min(idx / CPR, last), j = idx % CPR;
-        k[i] = *reinterpret_cast<const u32x4*>(K + ((t.row0 + key) * p.hkv + g) * D + 8 * j);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VL; ++i) {
-      const int it = tid + T * i;
-      if (VIT % T == 0 || it < VIT) {
-        const int q2 = it / CPR, j = it % CPR;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int key = min(2 * q2 + kk, last);
-          v[i][kk] = *reinterpret_cast<const u32x4*>(V + ((t.row0 + key) * p.hkv + g) * D + 8 * j);
-        }
+        const int64_t off = ((t.row0 + key) * p.hkv + g) * D + 8 * j;
+        k[i] = *reinterpret_cast<const u32x4*>(K + off);
+        v[i] = *reinterpret_cast<const u32x4*>(V + off);
       }
     }
   }
 
   __device__ __forceinline__ void store(uint16_t* lk, uint16_t* lv, int tid) const {
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
+    for (int i = 0; i < L; ++i) {
       const int idx = tid + T * i;
-      if (KCH % T == 0 || idx < KCH) {
-        const int key = idx / CPR, j = idx % CPR;
-        *reinterpret_cast<u32x4*>(lk + key * D + 8 * (j ^ (key & 7))) = k[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VL; ++i) {
-      const int it = tid + T * i;
-      if (VIT % T == 0 || it < VIT) {
-        const int q2 = it / CPR, j = it % CPR;
-        const int pos = vt_pos(2 * q2);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 8 * j + e;
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const uint32_t w = __builtin_amdgcn_perm(v[i][1][e >> 1], v[i][0][e >> 1], sel);
-          const int phys = (pos >> 3) ^ vt_swz(d);
-          *reinterpret_cast<uint32_t*>(lv + d * kTileKeys + 8 * phys + (pos & 7)) = w;
-        }
+      if (CH % T == 0 || idx < CH) {
+        LdsTile<D>::store(lk, idx / CPR, idx % CPR, k[i]);
+        LdsTile<D>::store(lv, idx / CPR, idx % CPR, v[i]);
       }
     }
   }
@@ -323,9 +285,7 @@ fwd_bf16_kernel(FwdParams p) {
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const int key = 32 * mt + l32;
-          const bf16x8 kf = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(lk + key * D + 8 * ((2 * ks + h2) ^ (key & 7))));
+          const bf16x8 kf = LdsTile<D>::frag(lk, 32 * mt + l32, 2 * ks + h2);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
             sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], sacc[mt][nt], 0, 0, 0);
@@ -396,9 +356,9 @@ fwd_bf16_kernel(FwdParams p) {
       for (int kq = 0; kq < 4; ++kq) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int d = 32 * dt + l32;
-          const bf16x8 vf = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(lv + d * kTileKeys + 8 * ((2 * kq + h2) ^ vt_swz(d))));
+          const int sl = lane & 15;
+          const bf16x8 vf = LdsTile<D>::frag_t(lv, tr_row_a(kq, h2, sl), tr_row_b(kq, h2, sl),
+                                               32 * dt + 16 * ((lane >> 4) & 1), sl);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
             oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nt][kq], oacc[dt][nt], 0, 0, 0);

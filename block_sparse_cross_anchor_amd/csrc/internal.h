@@ -39,7 +39,12 @@ struct AttnArgs {
   void* dk_self;
   void* dv_self;
   int32_t flags;  // SXA_BWD_* phases (never 0 here)
+  void* workspace;  // optional dK/dV split scratch (nullptr: no split)
+  int64_t workspace_bytes;
 };
+
+// Bytes of dK/dV split scratch for n_loc local rows (0 if not representable).
+int64_t bwd_workspace_bytes(int64_t n_loc, int32_t hkv, int32_t d);
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t s);

@@ -1,0 +1,61 @@
+// Row-major bf16 tiles in LDS and the two ways the MFMA kernels read them.
+//
+// A tile holds rows of D bf16 values (D / 8 chunks of 16 bytes).  The chunk index
+// is XOR-ed with the low bits of the row so that the 16 lanes that read 16
+// consecutive rows at one logical chunk touch 16 distinct chunk positions.
+//
+//  * frag(): one 16-byte read per lane -- row `row`, 8 consecutive columns
+//    starting at 8 * chunk.  Used for MFMA operands whose contraction index runs
+//    along the row (e.g. K or Q with the head dimension contracted).
+//  * frag_t(): the transposed operand.  gfx950's ds_read_b64_tr_b16 reads 8 bytes
+//    per lane and, inside each group of 16 lanes, hands output lane 4c + e the
+//    e-th 16-bit element of the reads of lanes c, c + 4, c + 8 and c + 12.  If lane
+//    s of the group points at row rows[s / 4], columns col + 4 * (s % 4) .. + 3,
+//    output lane i receives column col + i of rows rows[0..3].  Two such reads
+//    give a lane 8 rows of one column: the MFMA operand of X^T whose contraction
+//    index runs over rows (V^T for P V, K^T for dS K, Q^T / dO^T for dK / dV).
+#pragma once
+#include "device_common.h"
+
+namespace sxa {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int D>
+struct LdsTile {
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+
+  __device__ static __forceinline__ int phys(int row, int chunk) { return chunk ^ (row & (CPR - 1)); }
+
+  __device__ static __forceinline__ void store(uint16_t* t, int row, int chunk, const u32x4& v) {
+    *reinterpret_cast<u32x4*>(t + row * D + 8 * phys(row, chunk)) = v;
+  }
+
+  __device__ static __forceinline__ bf16x8 frag(const uint16_t* t, int row, int chunk) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(t + row * D + 8 * phys(row, chunk)));
+  }
+
+  // lane s (0..15) of its 16-lane group: rows r4[s / 4] of the first read and
+  // r4b[s / 4] of the second; columns col + 4 * (s % 4).  `col` is a multiple of 16.
+  __device__ static __forceinline__ bf16x8 frag_t(const uint16_t* t, int row_a, int row_b, int col, int s) {
+    const int c = col + 4 * (s & 3);
+    const int chunk = c >> 3, within = c & 7;
+    const uint16_t* pa = t + row_a * D + 8 * phys(row_a, chunk) + within;
+    const uint16_t* pb = t + row_b * D + 8 * phys(row_b, chunk) + within;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pb));
+    // combine through 32-bit words (element-wise __bf16 bit casts are not reliable)
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return __builtin_bit_cast(bf16x8, u32x4{ua[0], ua[1], ub[0], ub[1]});
+  }
+};
+
+// Key order shared by P (or dS) held in MFMA accumulator registers and the
+// transposed operand that multiplies it: in k-step ks (16 keys) lane half h holds,
+// at positions i = 0..7, the keys 16 ks + 8 (i / 4) + 4 h + i % 4.  frag_t reads
+// positions 0..3 from rows 16 ks + 4 h + (s / 4) and 4..7 from 16 ks + 8 + 4 h + (s / 4).
+__device__ __forceinline__ int tr_row_a(int ks, int h, int s) { return 16 * ks + 4 * h + (s >> 2); }
+__device__ __forceinline__ int tr_row_b(int ks, int h, int s) { return 16 * ks + 8 + 4 * h + (s >> 2); }
+
+}  // namespace sxa

@@ -22,8 +22,8 @@ SXA_OK, SXA_EINVAL, SXA_EUNSUPPORTED, SXA_EHIP = 0, -1, -2, -3
 BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_DQ_OVERWRITE = 1, 2, 4, 8
 BLOCK = 16
 
-EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_bwd", "lse_combine", "chunk_cost", "lpt_assign",
-           "context_gather", "sxa_last_error")
+EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_bwd", "sparse_xattn_bwd_workspace_bytes",
+           "lse_combine", "chunk_cost", "lpt_assign", "context_gather", "sxa_last_error")
 
 _lib = None
 
@@ -47,7 +47,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     attn_common = [P, P, P, ctypes.c_int, I32, I32, I32, I32, I32, F32, P, P, P, P, I32, I64, P, P]
     lib.sparse_xattn_fwd.argtypes = attn_common + [P, ctypes.c_int, P, P]
     lib.sparse_xattn_fwd.restype = ctypes.c_int
-    lib.sparse_xattn_bwd.argtypes = attn_common + [P, P, P, P, P, P, P, P, P, I32, P]
+    lib.sparse_xattn_bwd.argtypes = attn_common + [P, P, P, P, P, P, P, P, P, P, I64, I32, P]
+    lib.sparse_xattn_bwd_workspace_bytes.argtypes = [I64, I32, I32]
+    lib.sparse_xattn_bwd_workspace_bytes.restype = I64
     lib.sparse_xattn_bwd.restype = ctypes.c_int
     lib.lse_combine.argtypes = [P, ctypes.c_int, P, I32, I64, I32, P, ctypes.c_int, P, P]
     lib.lse_combine.restype = ctypes.c_int
@@ -143,12 +145,27 @@ def sparse_xattn_fwd(q, k, v, meta: Meta, scale: float, k_self=None, v_self=None
     return out, lse
 
 
+_workspaces = {}
+
+
+def bwd_workspace(n_loc: int, hkv: int, d: int, device) -> torch.Tensor:
+    """Scratch that lets the dK/dV phase split heavily read key tiles (cached per device;
+    grown on demand)."""
+    need = int(load_library().sparse_xattn_bwd_workspace_bytes(int(n_loc), int(hkv), int(d)))
+    key = torch.device(device)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=key)
+        _workspaces[key] = ws
+    return ws
+
+
 def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
                      k_self=None, v_self=None, delta_ws=None, dk=None, dv=None, dk_self=None,
-                     dv_self=None, flags: int = 0):
+                     dv_self=None, flags: int = 0, workspace="auto"):
     """Backward of the local chunks (+ own-block term).  Adds into dq_accum (float32)
     unless BWD_DQ_OVERWRITE is set; ``flags`` selects phases (0 = all).
-    Returns (dk, dv, dk_self, dv_self)."""
+    Returns the float32 gradients (dk, dv, dk_self, dv_self)."""
     n_q, hq, d = q.shape
     hkv = k.shape[1]
     _need(q, "q")
@@ -160,24 +177,32 @@ def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
     _need(dq_accum, "dq_accum", (n_q, hq, d), torch.float32)
     if delta_ws is None:
         delta_ws = torch.empty((n_q, hq), dtype=torch.float32, device=q.device)
+    f32 = torch.float32
     if dk is None:
-        dk = torch.empty_like(k)
+        dk = torch.empty(k.shape, dtype=f32, device=k.device)
     if dv is None:
-        dv = torch.empty_like(v)
+        dv = torch.empty(v.shape, dtype=f32, device=v.device)
+    _need(dk, "dk", k.shape, f32)
+    _need(dv, "dv", v.shape, f32)
     if k_self is not None:
         _need(k_self, "k_self", (n_q, hkv, d), q.dtype)
         _need(v_self, "v_self", (n_q, hkv, d), q.dtype)
         if dk_self is None:
-            dk_self = torch.empty_like(k_self)
+            dk_self = torch.empty(k_self.shape, dtype=f32, device=q.device)
         if dv_self is None:
-            dv_self = torch.empty_like(v_self)
+            dv_self = torch.empty(v_self.shape, dtype=f32, device=q.device)
+        _need(dk_self, "dk_self", k_self.shape, f32)
+        _need(dv_self, "dv_self", v_self.shape, f32)
     lib = load_library()
+    if isinstance(workspace, str):  # "auto"
+        workspace = bwd_workspace(meta.n_loc, hkv, d, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.sparse_xattn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), meta.n_blk, BLOCK, hq, hkv, d, float(scale),
         _ptr(meta.anchor), _ptr(meta.sample_start), _ptr(meta.chunk_gstart), _ptr(meta.chunk_len),
         meta.n_chunk, meta.n_loc, _ptr(k_self), _ptr(v_self), _ptr(o), _ptr(dout), _ptr(lse),
         _ptr(delta_ws), _ptr(dq_accum), _ptr(dk), _ptr(dv), _ptr(dk_self), _ptr(dv_self),
-        int(flags), _stream()))
+        _ptr(workspace), ws_bytes, int(flags), _stream()))
     return dk, dv, dk_self, dv_self
 
 

@@ -23,6 +23,7 @@
  *   q, o, dout, dq_accum : [n_q][hq][d]
  *   k, v, dk, dv          : [n_loc][hkv][d]   local rows = the listed chunks back to back
  *   k_self, v_self, dk_self, dv_self : [n_q][hkv][d]  keys/values of the draft tokens
+ *   (gradients dq_accum, dk, dv, dk_self, dv_self are always float32)
  *   lse, delta_ws         : [n_q][hq] float32
  * Query head h reads kv head h / (hq / hkv).
  * Metadata (device int32 arrays):
@@ -106,9 +107,14 @@ enum {
  *            call with the same o and dout may skip the phase).
  *   dq_accum [n_q][hq][d] float32: this call's query gradient is ADDED to it (or
  *            written, with SXA_BWD_DQ_OVERWRITE), so per-chunk calls accumulate.
- *   dk, dv   [n_loc][hkv][d] in in_dtype: overwritten.
- *   dk_self, dv_self [n_q][hkv][d] in in_dtype: overwritten when k_self != NULL
+ *   dk, dv   [n_loc][hkv][d] float32: overwritten.
+ *   dk_self, dv_self [n_q][hkv][d] float32: overwritten when k_self != NULL
  *            (must then be non-NULL), ignored otherwise.
+ *   workspace, workspace_bytes: optional device scratch for the bf16 dK/dV phase.
+ *            With at least sparse_xattn_bwd_workspace_bytes() bytes, key tiles that
+ *            many query blocks read are split over up to four workgroups whose
+ *            partial sums are added by a second pass; with NULL (or too small) every
+ *            key tile is handled by one workgroup.  Contents are scratch.
  *   flags    SXA_BWD_* bits selecting the phases; they run in the order
  *            DELTA, DQ, DKDV on `stream`.
  */
@@ -119,7 +125,12 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                      int64_t n_loc, const void* k_self, const void* v_self,
                      const void* o, const void* dout, const float* lse,
                      float* delta_ws, float* dq_accum, void* dk, void* dv,
-                     void* dk_self, void* dv_self, int32_t flags, void* stream);
+                     void* dk_self, void* dv_self, void* workspace, int64_t workspace_bytes,
+                     int32_t flags, void* stream);
+
+/* Workspace bytes that let sparse_xattn_bwd split heavily read key tiles
+ * (a function of n_loc, hkv and d only; 0 for invalid sizes). */
+int64_t sparse_xattn_bwd_workspace_bytes(int64_t n_loc, int32_t hkv, int32_t d);
 
 /*
  * Exact merge of n_parts partials from their log-sum-exp statistics

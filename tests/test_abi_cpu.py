@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "sxattn.h")
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
