@@ -189,6 +189,30 @@ def step(torch, P, T):
     return bins_np, load.numpy(), cost_np, bin_pairs
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_8kq_64k_8bins.md")
+KERNEL_SOURCE = {"sparse_xattn_fwd": "attn_fwd.hip", "bwd_dq": "attn_bwd.hip", "bwd_dkdv": "attn_bwd.hip"}
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
+    or None when the summary is missing or the kernel's source changed since."""
+    import hashlib
+
+    src = KERNEL_SOURCE.get(kernel)
+    if src is None or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line:
+            k, v = (x.strip() for x in line.split("=", 1))
+            vals[k] = v
+    path = os.path.join(ROOT, "block_sparse_cross_anchor_amd", "csrc", src)
+    if vals.get(src) != hashlib.sha256(open(path, "rb").read()).hexdigest():
+        return None
+    v = vals.get(f"{kernel}_bytes_per_launch")
+    return None if v is None else float(v)
+
+
 def cpu_baseline(P, seconds):
     """The oracle, as it stands, on a bounded sample of blocks of the same workload:
     forward then backward of the sampled blocks over the whole context."""
@@ -278,7 +302,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if is_mfma else PEAK_HBM_GBS
     roofline = {"bound": "mfma" if is_mfma else "hbm", "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s" if is_mfma else "GB/s",
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / peak, 4), "traffic": recorded_traffic(dom), "kernel": dom,
                 "avg_launch_ms": round(avg_ms, 4), "launches_per_step": a["launches"] // args.steps}
     kernels = {}
     for n, k in per_kernel.items():
