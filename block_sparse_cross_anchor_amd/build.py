@@ -42,14 +42,14 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, bdir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     if src.endswith(".cpp"):
         cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC, "-c", path,
                "-o", obj]
     else:
-        cmd = [_hipcc(), *HIPCC_FLAGS, "-c", path, "-o", obj]
+        cmd = [_hipcc(), *HIPCC_FLAGS, *extra, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -61,20 +61,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = True, out: str = OUT, defines=()) -> str:
+    """Compile every source and link `out`.  `defines` (e.g. ["SXA_KV_WAVES=4"]) are
+    passed to hipcc as -D flags, for building tuning variants out of tree."""
+    bdir = BUILD_DIR if out == OUT else out + "_objs"
+    os.makedirs(bdir, exist_ok=True)
     jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    extra = [f"-D{d}" for d in defines]
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, bdir, extra), SOURCES))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -28,8 +28,14 @@ namespace sxa {
 namespace {
 
 constexpr int kTileKeys = 64;
-constexpr int kWaves = 8;
-constexpr int kT = 64 * kWaves;
+#ifndef SXA_DQ_WAVES
+#define SXA_DQ_WAVES 8
+#endif
+#ifndef SXA_KV_WAVES
+#define SXA_KV_WAVES 8
+#endif
+constexpr int kDqWaves = SXA_DQ_WAVES;  // waves per dq workgroup (32 query rows each)
+constexpr int kKvWaves = SXA_KV_WAVES;  // waves per dkdv workgroup (32 keys each)
 
 struct BwdParams {
   const uint16_t* q;
@@ -121,7 +127,7 @@ __device__ __forceinline__ bool walk_next(Walk& w, const int32_t* __restrict__ c
 
 // K and V tiles staged row-major (lds_tile.h); K^T for dQ comes from the
 // transposing read of the same K tile.
-template <int D>
+template <int D, int kT>
 struct DqTileRegs {
   static constexpr int CPR = D / 8;
   static constexpr int CH = kTileKeys * CPR;
@@ -157,10 +163,12 @@ struct DqTileRegs {
 };
 
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_kernel(BwdParams p) {
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWaves))) void dq_bf16_kernel(
+    BwdParams p) {
+  constexpr int kT = 64 * kDqWaves;
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
-  constexpr int ROWS = 32 * kWaves;
+  constexpr int ROWS = 32 * kDqWaves;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileKeys * D];
 
   const int tid = threadIdx.x;
@@ -224,7 +232,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[dt][i] = 0.f;
 
-  DqTileRegs<D> regs;
+  DqTileRegs<D, kT> regs;
   regs.load(cur, p, g, tid);
   regs.store(lds[0][0], lds[0][1], tid);
   __syncthreads();
@@ -312,7 +320,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dq_bf16_ker
 // keys (own-block tiles: when it holds one of their blocks).  When the group size
 // is even a step lies inside one block, so its mask is one interval ("uniform").
 
-constexpr int kKeysPerWG = 32 * kWaves;
+constexpr int kKeysPerWG = 32 * kKvWaves;
 constexpr int kStepRows = 32;
 constexpr int kStepsPerPart = 112;  // query steps per workgroup above which a tile is split
 constexpr int kMaxParts = 4;
@@ -326,9 +334,11 @@ struct StepMeta {
 };
 
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kT, kT))) void dkdv_bf16_kernel(BwdParams p,
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWaves))) void dkdv_bf16_kernel(BwdParams p,
                                                                                       int n_ctx_tiles,
                                                                                       int n_tiles) {
+  constexpr int kT = 64 * kKvWaves;
+  constexpr int kWaves = kKvWaves;
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int CPR = D / 8;
@@ -682,8 +692,8 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   p.ws_slots = nullptr;
   if (a.flags & SXA_BWD_DQ) {
     const int64_t rows = static_cast<int64_t>(a.n_blk) * kBlock * (a.hq / a.hkv);
-    const int64_t n_dq = (rows + 32 * kWaves - 1) / (32 * kWaves) * a.hkv;
-    dq_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_dq)), dim3(kT), 0, s>>>(p);
+    const int64_t n_dq = (rows + 32 * kDqWaves - 1) / (32 * kDqWaves) * a.hkv;
+    dq_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_dq)), dim3(64 * kDqWaves), 0, s>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (!(a.flags & SXA_BWD_DKDV)) return hipSuccess;
@@ -699,7 +709,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
                                           ((n_ctx_tiles * a.hkv * 4 + 255) / 256) * 256);
   }
   const int64_t n_kv = n_tiles * a.hkv * (split ? kMaxParts : 1);
-  dkdv_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_kv)), dim3(kT), 0, s>>>(p, static_cast<int>(n_ctx_tiles),
+  dkdv_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_kv)), dim3(64 * kKvWaves), 0, s>>>(p, static_cast<int>(n_ctx_tiles),
                                                                             static_cast<int>(n_tiles));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (split && n_ctx_tiles > 0) {

@@ -39,6 +39,8 @@
 #include "internal.h"
 #include "lds_tile.h"
 
+#include <type_traits>
+
 namespace sxa {
 namespace {
 
@@ -103,8 +105,11 @@ __device__ __forceinline__ bool walk_next(Walk& w, const int32_t* __restrict__ c
       w.len = 0;
       return false;
     }
-    w.gs = cgs[w.c];
-    w.len = clen[w.c];
+    // uniform index + constant address space: scalar loads, counted apart from
+    // the vector-memory queue that the tile DMA uses
+    const int c = __builtin_amdgcn_readfirstlane(w.c);
+    w.gs = ((const __attribute__((address_space(4))) int32_t*)(cgs))[c];
+    w.len = ((const __attribute__((address_space(4))) int32_t*)(clen))[c];
     const int a = max(LO, w.gs), e = min(HI, w.gs + w.len);
     if (a < e) {
       w.t = (a - w.gs) / kTileKeys;
@@ -117,41 +122,35 @@ __device__ __forceinline__ bool walk_next(Walk& w, const int32_t* __restrict__ c
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
-// Staging of one 64-key tile (K and V rows of one kv head) through registers into
-// row-major LDS tiles, split over all T threads of the workgroup.
-template <int D, int T>
-struct TileRegs {
-  static constexpr int CPR = D / 8;            // 16-byte chunks per row
-  static constexpr int CH = kTileKeys * CPR;   // chunks per tensor
-  static constexpr int L = (CH + T - 1) / T;
-  u32x4 k[L], v[L];
+// One 64-key tile (K rows then V rows of one kv head) is copied straight from HBM
+// into a row-major LDS tile with global_load_lds_dwordx4: lane i of a wave writes
+// the 16 bytes at LDS offset 16 i of its 1 KiB slice, so each lane picks the
+// global chunk that belongs at that position under the tile's swizzle.  Rows past
+// the tile end are clamped to its last row (those keys are masked, any finite
+// value will do).  Every wave issues NI instructions per tile.
+template <int D, int WAVES>
+struct TileDma {
+  static constexpr int CPR = D / 8;
+  static constexpr int HALF = kTileKeys * CPR;   // chunks of K (or V) per tile
+  static constexpr int NI = 2 * HALF / 64 / WAVES;
+  static_assert(NI * 64 * WAVES == 2 * HALF, "tile must split evenly over the waves");
+  static constexpr int ELEMS = 2 * kTileKeys * D;  // bf16 per buffer
 
-  // Rows past the tile end are clamped to its last row: those keys are masked, so
-  // any finite value will do and the loads stay branch-free.
-  __device__ __forceinline__ void load(const Tile& t, const FwdParams& p, int g, int tid) {
+  __device__ static __forceinline__ void issue(const Tile& t, const FwdParams& p, int g, int wave,
+                                               int lane, uint16_t* buf) {
     const uint16_t* K = t.self ? p.k_self : p.k;
     const uint16_t* V = t.self ? p.v_self : p.v;
     const int last = t.nrows - 1;
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int idx = tid + T * i;
-      if (CH % T == 0 || idx < CH) {
-        const int key = min(idx / CPR, last), j = idx % CPR;
-        const int64_t off = ((t.row0 + key) * p.hkv + g) * D + 8 * j;
-        k[i] = *reinterpret_cast<const u32x4*>(K + off);
-        v[i] = *reinterpret_cast<const u32x4*>(V + off);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* lk, uint16_t* lv, int tid) const {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int idx = tid + T * i;
-      if (CH % T == 0 || idx < CH) {
-        LdsTile<D>::store(lk, idx / CPR, idx % CPR, k[i]);
-        LdsTile<D>::store(lv, idx / CPR, idx % CPR, v[i]);
-      }
+    for (int j = 0; j < NI; ++j) {
+      const int inst = wave * NI + j;
+      const int c = inst * 64 + lane;
+      const bool isv = c >= HALF;  // uniform per instruction
+      const int cc = isv ? c - HALF : c;
+      const int row = cc / CPR;
+      const int logical = (cc % CPR) ^ LdsTile<D>::swz(row);
+      const uint16_t* src = (isv ? V : K) + ((t.row0 + min(row, last)) * p.hkv + g) * D + 8 * logical;
+      dma16(src, lds_addr(buf + inst * 512));
     }
   }
 };
@@ -164,7 +163,8 @@ fwd_bf16_kernel(FwdParams p) {
   constexpr int ROWS = 32 * NT * WAVES;  // rows per workgroup
   constexpr int KS = D / 16;             // k-steps of S^T
   constexpr int DT = D / 32;             // 32-row d tiles of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileKeys * D];
+  using Dma = TileDma<D, WAVES>;
+  __shared__ __attribute__((aligned(16))) uint16_t bufs[3][Dma::ELEMS];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
@@ -249,128 +249,137 @@ fwd_bf16_kernel(FwdParams p) {
     }
   }
 
-  TileRegs<D, T> regs;
-  regs.load(cur, p, g, tid);
-  regs.store(lds[0][0], lds[0][1], tid);
-  __syncthreads();
-  int buf = 0;
+  // Three-stage pipeline: tile t is computed from buffer t % 3 while the DMA of
+  // tiles t + 1 and t + 2 is in flight.  The prologue's own loads complete first,
+  // so that the only vector-memory operations in flight in the loop are the DMA.
+  wait_vmcnt<0>();
+  Tile n1, n2;
+  Dma::issue(cur, p, g, wave, lane, bufs[0]);
+  bool have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
+  if (have1) Dma::issue(n1, p, g, wave, lane, bufs[1]);
+  int cb = 0;
   while (true) {
-    const bool has_next = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, nxt);
-    if (has_next) regs.load(nxt, p, g, tid);
-
-    // ---- this wave's share of the tile
-    int a_lo[NT], a_hi[NT];
-    bool any = false, full = true;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int lo = cur.self ? slo[nt] : clo[nt];
-      const int hi = cur.self ? shi[nt] : chi[nt];
-      a_lo[nt] = max(lo - cur.coord0, 0);
-      a_hi[nt] = min(hi - cur.coord0, cur.nrows);
-      any |= a_lo[nt] < a_hi[nt];
-      full &= (a_lo[nt] == 0) & (a_hi[nt] == kTileKeys);
-    }
-    if (__any(any)) {
-      const bool all_full = __all(full);
-      const uint16_t* lk = lds[buf][0];
-      const uint16_t* lv = lds[buf][1];
-      f32x16 sacc[2][NT];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[mt][nt][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 kf = LdsTile<D>::frag(lk, 32 * mt + l32, 2 * ks + h2);
-#pragma unroll
+    const uint16_t* cbuf = bufs[cb];
+    uint16_t* pbuf = bufs[cb == 0 ? 2 : cb - 1];
+    if (have1) wait_vmcnt<Dma::NI>();  // this wave's DMA of `cur` done (n1 may be in flight)
+    else wait_vmcnt<0>();
+    barrier_nofence();                 // ... and every wave's; all reads of pbuf are done
+    const bool have2 = have1 && walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);
+    if (have2) Dma::issue(n2, p, g, wave, lane, pbuf);
+      // ---- this wave's share of the tile
+      int a_lo[NT], a_hi[NT];
+      bool any = false, full = true;
+  #pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int lo = cur.self ? slo[nt] : clo[nt];
+        const int hi = cur.self ? shi[nt] : chi[nt];
+        a_lo[nt] = max(lo - cur.coord0, 0);
+        a_hi[nt] = min(hi - cur.coord0, cur.nrows);
+        any |= a_lo[nt] < a_hi[nt];
+        full &= (a_lo[nt] == 0) & (a_hi[nt] == kTileKeys);
+      }
+      if (__any(any)) {
+        const bool all_full = __all(full);
+        const uint16_t* lk = cbuf;
+        const uint16_t* lv = cbuf + kTileKeys * D;
+        f32x16 sacc[2][NT];
+  #pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
-            sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], sacc[mt][nt], 0, 0, 0);
-        }
-      }
-      bf16x8 pf[NT][4];
-      bool need[NT];
-      float tmax[NT];
-      bool any_need = false;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (!all_full) {
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = 32 * mt + 8 * (r / 4) + 4 * h2 + (r % 4);
-              if (key < a_lo[nt] || key >= a_hi[nt]) sacc[mt][nt][r] = -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
-        mx = fmaxf(mx, swap_halves(mx)) * p.scale_log2;
-        need[nt] = mx > m[nt] + kRescaleSlack;
-        tmax[nt] = mx;
-        any_need |= need[nt];
-      }
-      // Lazy rescale: the running max of a column only moves when the tile max
-      // exceeds it by more than kRescaleSlack (so p <= 2^kRescaleSlack); the O
-      // accumulators are rescaled only then, for the whole wave at once.
-      if (__any(any_need)) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const float mnew = need[nt] ? tmax[nt] : m[nt];
-          const float alpha =
-              need[nt] ? (m[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[nt] - mnew)) : 1.f;
-          m[nt] = mnew;
-          l[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float muse = m[nt] == -INFINITY ? 0.f : m[nt];
-        float rs = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], p.scale_log2, -muse));
-            sacc[mt][nt][r] = e;
-            rs += e;
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[mt][nt][r] = 0.f;
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+  #pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const bf16x8 kf = LdsTile<D>::frag(lk, 32 * mt + l32, 2 * ks + h2);
+  #pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], sacc[mt][nt], 0, 0, 0);
           }
-        l[nt] += rs;
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            pf[nt][kq][i] = static_cast<__bf16>(sacc[kq / 2][nt][8 * (kq % 2) + i]);
-      }
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int sl = lane & 15;
-          const bf16x8 vf = LdsTile<D>::frag_t(lv, tr_row_a(kq, h2, sl), tr_row_b(kq, h2, sl),
-                                               32 * dt + 16 * ((lane >> 4) & 1), sl);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nt][kq], oacc[dt][nt], 0, 0, 0);
+        }
+        bf16x8 pf[NT][4];
+        bool need[NT];
+        float tmax[NT];
+        bool any_need = false;
+  #pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if (!all_full) {
+  #pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = 32 * mt + 8 * (r / 4) + 4 * h2 + (r % 4);
+                if (key < a_lo[nt] || key >= a_hi[nt]) sacc[mt][nt][r] = -INFINITY;
+              }
+          }
+          float mx = -INFINITY;
+  #pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
+          mx = fmaxf(mx, swap_halves(mx)) * p.scale_log2;
+          need[nt] = mx > m[nt] + kRescaleSlack;
+          tmax[nt] = mx;
+          any_need |= need[nt];
+        }
+        // Lazy rescale: the running max of a column only moves when the tile max
+        // exceeds it by more than kRescaleSlack (so p <= 2^kRescaleSlack); the O
+        // accumulators are rescaled only then, for the whole wave at once.
+        if (__any(any_need)) {
+  #pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const float mnew = need[nt] ? tmax[nt] : m[nt];
+            const float alpha =
+                need[nt] ? (m[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[nt] - mnew)) : 1.f;
+            m[nt] = mnew;
+            l[nt] *= alpha;
+  #pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
+          }
+        }
+  #pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float muse = m[nt] == -INFINITY ? 0.f : m[nt];
+          float rs = 0.f;
+  #pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float e = __builtin_amdgcn_exp2f(fmaf(sacc[mt][nt][r], p.scale_log2, -muse));
+              sacc[mt][nt][r] = e;
+              rs += e;
+            }
+          l[nt] += rs;
+  #pragma unroll
+          for (int kq = 0; kq < 4; ++kq)
+  #pragma unroll
+            for (int i = 0; i < 8; ++i)
+              pf[nt][kq][i] = static_cast<__bf16>(sacc[kq / 2][nt][8 * (kq % 2) + i]);
+        }
+  #pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+  #pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int sl = lane & 15;
+            const bf16x8 vf = LdsTile<D>::frag_t(lv, tr_row_a(kq, h2, sl), tr_row_b(kq, h2, sl),
+                                                 32 * dt + 16 * ((lane >> 4) & 1), sl);
+  #pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nt][kq], oacc[dt][nt], 0, 0, 0);
+          }
         }
       }
-    }
 
-    if (has_next) regs.store(lds[buf ^ 1][0], lds[buf ^ 1][1], tid);
-    __syncthreads();
-    if (!has_next) break;
-    cur = nxt;
-    buf ^= 1;
+
+    if (!have1) break;
+    cur = n1;
+    n1 = n2;
+    have1 = have2;
+    cb = cb == 2 ? 0 : cb + 1;
   }
 
   // ---- epilogue: normalise, write O and lse
@@ -400,8 +409,11 @@ fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-constexpr int kNT = 1;      // 32 query rows per wave
-constexpr int kWaves = 8;   // 8 waves (2 per SIMD) share each K/V tile
+#ifndef SXA_FWD_WAVES
+#define SXA_FWD_WAVES 8
+#endif
+constexpr int kNT = 1;                  // 32 query rows per wave
+constexpr int kWaves = SXA_FWD_WAVES;   // waves sharing each K/V tile
 constexpr int kRowsPerWG = 32 * kNT * kWaves;
 
 template <int D, bool OUT_BF16>

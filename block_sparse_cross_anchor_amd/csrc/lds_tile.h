@@ -1,8 +1,8 @@
 // Row-major bf16 tiles in LDS and the two ways the MFMA kernels read them.
 //
 // A tile holds rows of D bf16 values (D / 8 chunks of 16 bytes).  The chunk index
-// is XOR-ed with the low bits of the row so that the 16 lanes that read 16
-// consecutive rows at one logical chunk touch 16 distinct chunk positions.
+// is XOR-ed with a function of the row (swz) chosen so that both read patterns
+// below are free of LDS bank conflicts (checked with SQ_LDS_BANK_CONFLICT).
 //
 //  * frag(): one 16-byte read per lane -- row `row`, 8 consecutive columns
 //    starting at 8 * chunk.  Used for MFMA operands whose contraction index runs
@@ -26,7 +26,15 @@ template <int D>
 struct LdsTile {
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
 
-  __device__ static __forceinline__ int phys(int row, int chunk) { return chunk ^ (row & (CPR - 1)); }
+  // Chunk swizzle f(row): a bijection on the low row bits, so 16 lanes reading 16
+  // consecutive rows at one chunk hit 16 distinct chunk positions; and the 4
+  // consecutive rows of one transposing read land in 4 different groups of 4
+  // chunks, so its 4 rows x 4 chunks (32 lanes) cover every bank once.
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);  // 128-byte rows: two per bank sweep
+  }
+  __device__ static __forceinline__ int phys(int row, int chunk) { return chunk ^ swz(row); }
 
   __device__ static __forceinline__ void store(uint16_t* t, int row, int chunk, const u32x4& v) {
     *reinterpret_cast<u32x4*>(t + row * D + 8 * phys(row, chunk)) = v;
@@ -57,5 +65,43 @@ struct LdsTile {
 // positions 0..3 from rows 16 ks + 4 h + (s / 4) and 4..7 from 16 ks + 8 + 4 h + (s / 4).
 __device__ __forceinline__ int tr_row_a(int ks, int h, int s) { return 16 * ks + 4 * h + (s >> 2); }
 __device__ __forceinline__ int tr_row_b(int ks, int h, int s) { return 16 * ks + 8 + 4 * h + (s >> 2); }
+
+// 16-byte direct HBM -> LDS copy (global_load_lds_dwordx4): lane i of the wave
+// writes LDS bytes [lds_base + 16 i, +16).  Issued from asm so that the compiler
+// does not add its own conservative waits for it; the caller waits with
+// wait_vmcnt<>() and a bare s_barrier before any wave reads the destination.
+// The instruction writes no VGPR, so nothing in flight can clobber a register.
+// m0 (which the compiler reserves) is saved and restored around it.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);  // wave-uniform by contract
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(base)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
+}
+
+// Wait until at most VM vector-memory operations of this wave are outstanding.
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without a memory fence (the fence of __syncthreads would also
+// wait for every DMA still in flight).  LDS written by ds_write must be waited for
+// (lgkmcnt) by the writer before it.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 }  // namespace sxa

@@ -34,11 +34,13 @@ class SxaError(RuntimeError):
         self.status = status
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libsxattn.so and declare the prototypes of every exported entry point."""
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libsxattn.so (or the build named by $SXATTN_LIB) and declare the prototypes
+    of every exported entry point."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("SXATTN_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m block_sparse_cross_anchor_amd.build`")
