@@ -115,7 +115,7 @@ def build_problem(torch, seed):
     P["lse_parts"] = torch.empty((nb, n_q, hq), dtype=f32, device="cuda")
     P["o"] = torch.empty((n_q * hq, d), dtype=bf, device="cuda")
     P["lse"] = torch.empty((n_q * hq,), dtype=f32, device="cuda")
-    P["delta"] = torch.empty((n_q, hq), dtype=f32, device="cuda")
+    P["delta"] = torch.empty((2, n_q, hq), dtype=f32, device="cuda")
     P["dq"] = torch.empty((n_q, hq, d), dtype=f32, device="cuda")
     P["cost"] = torch.empty((w.n_chunk,), dtype=torch.int64, device="cuda")
     P["plan_gs"] = torch.empty((nb, per_bin), dtype=torch.int32, device="cuda")

@@ -58,6 +58,8 @@ int check_attn(const void* q, const void* k, const void* v, sxa_dtype in_dtype, 
   if (n_chunk == 0 && n_loc != 0) return fail(SXA_EINVAL, "n_loc must be 0 when n_chunk is 0");
   if (static_cast<int64_t>(n_blk) * sxa::kBlock * hq * d >= (int64_t{1} << 40))
     return fail(SXA_EINVAL, "query tensor too large");
+  if (static_cast<int64_t>(n_blk) * sxa::kBlock * hq >= (int64_t{1} << 29))
+    return fail(SXA_EUNSUPPORTED, "n_blk * 16 * hq must be below 2^29 query rows");
   if ((k_self == nullptr) != (v_self == nullptr))
     return fail(SXA_EINVAL, "k_self and v_self must be both NULL or both non-NULL");
   if (n_blk > 0 && (q == nullptr || anchor == nullptr || sample_start == nullptr))
@@ -148,7 +150,7 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
   a.dv_self = dv_self;
   a.flags = flags;
   if (workspace_bytes < 0) return fail(SXA_EINVAL, "workspace_bytes must be >= 0");
-  const int64_t need = sxa::bwd_workspace_bytes(n_loc, hkv, d);
+  const int64_t need = sxa::bwd_workspace_bytes(n_blk, n_loc, hkv, d);
   a.workspace = (workspace != nullptr && need > 0 && workspace_bytes >= need) ? workspace : nullptr;
   a.workspace_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -164,9 +166,9 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                     "sparse_xattn_bwd launch");
 }
 
-int64_t sparse_xattn_bwd_workspace_bytes(int64_t n_loc, int32_t hkv, int32_t d) {
-  if (n_loc < 0 || hkv <= 0 || (d != 64 && d != 128)) return 0;
-  return sxa::bwd_workspace_bytes(n_loc, hkv, d);
+int64_t sparse_xattn_bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hkv, int32_t d) {
+  if (n_blk < 0 || n_loc < 0 || hkv <= 0 || (d != 64 && d != 128)) return 0;
+  return sxa::bwd_workspace_bytes(n_blk, n_loc, hkv, d);
 }
 
 int lse_combine(const void* o_parts, sxa_dtype part_dtype, const float* lse_parts,

@@ -31,11 +31,12 @@ constexpr int kTileKeys = 64;
 #ifndef SXA_DQ_WAVES
 #define SXA_DQ_WAVES 8
 #endif
-#ifndef SXA_KV_WAVES
-#define SXA_KV_WAVES 8
+#ifndef SXA_KV_HALVES
+#define SXA_KV_HALVES 1
 #endif
 constexpr int kDqWaves = SXA_DQ_WAVES;  // waves per dq workgroup (32 query rows each)
-constexpr int kKvWaves = SXA_KV_WAVES;  // waves per dkdv workgroup (32 keys each)
+constexpr int kKvHalves = SXA_KV_HALVES;    // 32-key halves per dkdv wave
+constexpr int kKvWaves = 8 / kKvHalves;      // waves per dkdv workgroup (256 keys)
 
 struct BwdParams {
   const uint16_t* q;
@@ -45,7 +46,7 @@ struct BwdParams {
   const uint16_t* v_self;
   const uint16_t* dout;
   const float* lse;
-  const float* delta;
+  const float* delta;  // [2][n_q][hq]: delta rows, then lse * log2(e) (+inf where lse = -inf)
   float* dq;
   float* dk;
   float* dv;
@@ -60,14 +61,18 @@ struct BwdParams {
   float scale;
   float scale_log2;  // scale * log2(e)
   int32_t dq_overwrite;
-  int32_t* ws_parts;  // dK/dV split scratch: parts per (context tile, kv head), or nullptr
-  float* ws_slots;    // [tile][hkv][kMaxParts][keys per tile][2][D] partial dK, dV
 };
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16_bits(a)) | (static_cast<uint32_t>(f32_to_bf16_bits(b)) << 16);
+  bf16x2 v;
+  v[0] = static_cast<__bf16>(a);
+  v[1] = static_cast<__bf16>(b);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ============================================================================ dq kernel
@@ -311,349 +316,587 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
 
 // ============================================================================ dkdv kernel
 //
-// Workgroup: 8 waves x 32 keys = 256 consecutive key rows of one kv head (local
-// context rows, or own-block rows for the tiles after the context ones).  K of a
-// wave's keys is held in registers (MFMA B operand of S = Q K^T); V of the
-// workgroup's keys sits in LDS (B operand of dP = dO V^T).  Query rows of kv head
-// g are numbered r = token * grp + (h - g*grp) and visited in steps of 32 rows;
-// a step is visited when one of its blocks' key intervals meets the workgroup's
-// keys (own-block tiles: when it holds one of their blocks).  When the group size
-// is even a step lies inside one block, so its mask is one interval ("uniform").
+// Key-major.  A workgroup of kKvWaves waves handles 32 keys per wave, i.e. a "key
+// tile" of 256 consecutive key rows of one kv head (local context rows, or own-block
+// rows for the tiles after the context ones).  K of a wave's keys is held in
+// registers (MFMA B operand of S = Q K^T); V of the tile sits in LDS (B operand of
+// dP = dO V^T).
+//
+// Query side.  The grp query heads of kv head g are visited in "steps" of 32 query
+// rows that start on a token boundary: ts = 32 / grp whole tokens with all their
+// heads when grp <= 32 (rows past ts grp are padding), or 32 heads of one token when
+// grp > 32.  Row i of a step is token tok0 + i / gs, head h0 + i % gs of the group
+// (gs = min(grp, 32)), so every lane copies from a fixed offset to the step's first
+// element.  A step covers at most 32 tokens and starts on a multiple of ts, so it
+// meets at most two 16-token blocks; its mask is two key intervals split at a row.
+// A step "hits" a tile when one of its blocks' intervals meets the tile's
+// key-coordinate range (own-block tiles: when it holds one of their blocks).
+//
+// Schedule.  The work is the list of (kv head, tile, hit step) triples, and a key
+// tile near the start of a long sample is hit by many times more steps than the
+// average one.  With a workspace, a count pass gives every tile its number of hit
+// steps and the kernel runs one workgroup per compute unit, each taking an equal
+// contiguous share of the list ("stream-K"): inside a share only the first and the
+// last tile can be partial; their fp32 sums go to the share's two workspace slots and
+// a reduce pass adds the slots of each such tile.  Tiles a share covers whole are
+// written directly.  Without a workspace every (tile, kv head) gets one workgroup.
+//
+// Pipeline.  The Q and dO rows of a step, and its per-row lse and delta, are copied
+// from HBM straight into LDS (global_load_lds), three steps deep: while step i is
+// computed the copies of steps i+1 and i+2 are in flight; one barrier per step.
 
-constexpr int kKeysPerWG = 32 * kKvWaves;
+constexpr int kKeysPerWave = 32 * kKvHalves;
+constexpr int kKeysPerWG = kKeysPerWave * kKvWaves;
 constexpr int kStepRows = 32;
-constexpr int kStepsPerPart = 112;  // query steps per workgroup above which a tile is split
-constexpr int kMaxParts = 4;
+constexpr int kListCap = 2 * 64 * kKvWaves;  // step indices held in LDS at once
 
-struct StepMeta {
-  float lse2[kStepRows];  // log2-domain lse per row (+inf: row contributes nothing)
-  float dlt[kStepRows];   // delta per row
-  int lo[kStepRows];      // per-row allowed key interval (non-uniform steps)
-  int hi[kStepRows];
-  int uni, lo0, hi0;      // uniform step: one interval for all rows
+struct DkdvSched {
+  int32_t n_ctx_tiles, n_tiles;
+  int32_t n_shares;        // stream-K workgroups; 0: one workgroup per (tile, kv head)
+  const int32_t* prefix;   // [n_tiles + 1]: first list position of each tile (per kv head)
+  const int32_t* krange;   // [n_tiles][2]: key-coordinate range of each tile
+  float* slots;            // [2 n_shares][kKeysPerWG][2][D]: partial dK, dV
 };
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWaves))) void dkdv_bf16_kernel(BwdParams p,
-                                                                                      int n_ctx_tiles,
-                                                                                      int n_tiles) {
-  constexpr int kT = 64 * kKvWaves;
-  constexpr int kWaves = kKvWaves;
-  constexpr int KS = D / 16;
-  constexpr int DT = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int SCH = 2 * kStepRows * CPR;  // 16-byte chunks of Q and dO rows of one step
-  constexpr int SL = (SCH + kT - 1) / kT;
-  __shared__ __attribute__((aligned(16))) uint16_t vtile[kKeysPerWG * D];
-  // per stage: Q and dO rows of the step, row-major (transposed operands via tr reads)
-  __shared__ __attribute__((aligned(16))) uint16_t stg[2][2][kStepRows * D];
-  __shared__ __attribute__((aligned(16))) StepMeta meta[2];
-  __shared__ int step_list[kT];
-  __shared__ int wave_cnt[kWaves];
-  __shared__ int red[2][kWaves];
-
-  const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
-  // blockIdx -> (part, tile, kv head); all first parts are dispatched first
-  const int per_part = n_tiles * p.hkv;
-  const int part = blockIdx.x / per_part;
-  const int g = (blockIdx.x % per_part) % p.hkv;
-  const int tile = (blockIdx.x % per_part) / p.hkv;
-  const bool self_tile = tile >= n_ctx_tiles;
-  const int grp = p.hq / p.hkv;
-  const int64_t n_q = static_cast<int64_t>(p.n_blk) * kBlock;
-  const int64_t R = n_q * grp;
-  const int64_t n_steps = (R + kStepRows - 1) / kStepRows;
-  const int64_t key_rows = self_tile ? n_q : p.n_loc;
-  const int64_t krow0 = static_cast<int64_t>(self_tile ? tile - n_ctx_tiles : tile) * kKeysPerWG;
-  const uint16_t* K = self_tile ? p.k_self : p.k;
-  const uint16_t* V = self_tile ? p.v_self : p.v;
-
-  // this lane's key (column of the S tile): local row and key coordinate
-  const int krow = 32 * wave + l32;
-  const int64_t kr = krow0 + krow;
-  const bool kvalid = kr < key_rows;
-  const int64_t krc = kvalid ? kr : key_rows - 1;
-  int kcoord = 0;  // global position (context) or own-block row (self)
-  if (self_tile) {
-    kcoord = static_cast<int>(krc);
-  } else {
-    int64_t off = 0;
-    for (int c = 0; c < p.n_chunk; ++c) {
-      const int len = p.chunk_len[c];
-      if (krc < off + len) {
-        kcoord = p.chunk_gstart[c] + static_cast<int>(krc - off);
-        break;
-      }
-      off += len;
-    }
+// Query-step geometry of one kv head's grp query heads.
+struct StepGeo {
+  int gs;   // heads per token inside a step: min(grp, 32)
+  int ts;   // tokens per step
+  int hcs;  // steps per token (head chunks): 1 when grp <= 32
+  int n_steps;
+  __device__ StepGeo(int grp, int n_q) {
+    gs = min(grp, kStepRows);
+    ts = kStepRows / gs;
+    hcs = (grp + kStepRows - 1) / kStepRows;
+    n_steps = (n_q + ts - 1) / ts * hcs;
   }
-  // key-coordinate range of the workgroup
-  int kmin = kvalid ? kcoord : 0x7fffffff, kmax = kvalid ? kcoord : -0x7fffffff;
+  __device__ int tok0(int st) const { return (st / hcs) * ts; }
+  __device__ int h0(int st) const { return (st % hcs) * kStepRows; }
+  __device__ int ntok(int st, int n_q) const { return min(ts, n_q - tok0(st)); }
+  // valid rows of a step (a prefix of its 32 rows)
+  __device__ int rows(int st, int n_q, int grp) const {
+    return hcs == 1 ? ntok(st, n_q) * gs : min(kStepRows, grp - h0(st));
+  }
+};
+
+__device__ __forceinline__ int ld_uniform(const int32_t* ptr, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)(ptr))[i];
+}
+
+// global key coordinate of local context row `krc` (own-block tiles: the row itself)
+__device__ __forceinline__ int key_coord(const BwdParams& p, bool self_tile, int64_t krc) {
+  if (self_tile) return static_cast<int>(krc);
+  int64_t off = 0;
+  for (int c = 0; c < p.n_chunk; ++c) {
+    const int len = p.chunk_len[c];
+    if (krc < off + len) return p.chunk_gstart[c] + static_cast<int>(krc - off);
+    off += len;
+  }
+  return 0;
+}
+
+__device__ __forceinline__ bool step_hit(const BwdParams& p, const StepGeo& sg, int st, int n_q,
+                                         bool self_tile, int kmin, int kmax) {
+  if (st >= sg.n_steps) return false;
+  const int t0 = sg.tok0(st);
+  const int b0 = t0 / kBlock, b1 = (t0 + sg.ntok(st, n_q) - 1) / kBlock;
+  bool hit = false;
+  for (int b = b0; b <= b1; ++b) {
+    const int lo = self_tile ? kBlock * b : p.sample_start[b];
+    const int hi = self_tile ? kBlock * b + kBlock : p.anchor[b];
+    hit |= (lo <= kmax) && (hi > kmin);
+  }
+  return hit;
+}
+
+// Count pass: one workgroup (256 threads, one per key row) per tile.
+__global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched sc, int32_t* prefix,
+                                                         int32_t* krange) {
+  __shared__ int red[2][4];
+  const int t = blockIdx.x, tid = threadIdx.x, wave = tid / 64;
+  const bool self_tile = t >= sc.n_ctx_tiles;
+  const int n_q = p.n_blk * kBlock;
+  const StepGeo sg(p.hq / p.hkv, n_q);
+  const int64_t key_rows = self_tile ? n_q : p.n_loc;
+  const int64_t kr = static_cast<int64_t>(self_tile ? t - sc.n_ctx_tiles : t) * kKeysPerWG + tid;
+  const bool valid = kr < key_rows;
+  const int c = valid ? key_coord(p, self_tile, kr) : 0;
+  int kmin = valid ? c : 0x7fffffff, kmax = valid ? c : -0x7fffffff;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     kmin = min(kmin, __shfl_xor(kmin, off, 64));
     kmax = max(kmax, __shfl_xor(kmax, off, 64));
   }
-  if (lane == 0) {
+  if (tid % 64 == 0) {
     red[0][wave] = kmin;
     red[1][wave] = kmax;
   }
   __syncthreads();
-  kmin = red[0][0];
-  kmax = red[1][0];
-#pragma unroll
-  for (int w2 = 1; w2 < kWaves; ++w2) {
-    kmin = min(kmin, red[0][w2]);
-    kmax = max(kmax, red[1][w2]);
+  kmin = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
+  kmax = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+  int n = 0;
+  for (int base = 0; base < sg.n_steps; base += 256)
+    n += __syncthreads_count(step_hit(p, sg, base + tid, n_q, self_tile, kmin, kmax));
+  if (tid == 0) {
+    prefix[t + 1] = n;
+    krange[2 * t] = kmin;
+    krange[2 * t + 1] = kmax;
+    if (t == 0) prefix[0] = 0;
   }
-
-  f32x16 dkacc[DT], dvacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dkacc[dt][i] = dvacc[dt][i] = 0.f;
-
-  // staging: chunk idx = tid + kT * i of [tensor (Q, dO)][row][chunk]
-  u32x4 sreg[SL];
-
-  auto row_off = [&](int64_t row) -> int64_t {  // element offset of query row `row`
-    const int64_t tk = row / grp;
-    return (tk * p.hq + static_cast<int64_t>(g) * grp + row % grp) * D;
-  };
-  // metadata of the staged step, prefetched with the rows: threads < 32 hold their
-  // row's lse / delta / interval, thread 32 the step's first block interval
-  float m_lse = 0.f, m_dlt = 0.f;
-  int m_lo = 0, m_hi = 0, m_uni = 0;
-  auto load_step = [&](int64_t step) {
-#pragma unroll
-    for (int i = 0; i < SL; ++i) {
-      const int idx = tid + kT * i;
-      if (SCH % kT == 0 || idx < SCH) {
-        const int tensor = idx / (kStepRows * CPR), rem = idx % (kStepRows * CPR);
-        const int64_t row = min(step * kStepRows + rem / CPR, R - 1);
-        sreg[i] = *reinterpret_cast<const u32x4*>((tensor == 0 ? p.q : p.dout) + row_off(row) + 8 * (rem % CPR));
-      }
-    }
-    if (tid < kStepRows) {
-      const int64_t row_raw = step * kStepRows + tid;
-      const bool rv = row_raw < R;
-      const int64_t row = rv ? row_raw : R - 1;
-      const int64_t tk = row / grp;
-      const int bb = static_cast<int>(tk / kBlock);
-      const int64_t li = tk * p.hq + static_cast<int64_t>(g) * grp + row % grp;
-      const float ln = p.lse[li];
-      m_lse = (rv && ln != -INFINITY) ? ln * kLog2e : INFINITY;
-      m_dlt = p.delta[li];
-      m_lo = self_tile ? kBlock * bb : p.sample_start[bb];
-      m_hi = rv ? (self_tile ? kBlock * bb + kBlock : p.anchor[bb]) : -0x7fffffff;
-    } else if (tid == kStepRows) {
-      const int64_t r0 = step * kStepRows, r1 = r0 + kStepRows - 1;
-      const int b0 = static_cast<int>(r0 / grp / kBlock);
-      m_uni = r1 < R && static_cast<int>(r1 / grp / kBlock) == b0;
-      m_lo = self_tile ? kBlock * b0 : p.sample_start[b0];
-      m_hi = self_tile ? kBlock * b0 + kBlock : p.anchor[b0];
-    }
-  };
-  auto store_step = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < SL; ++i) {
-      const int idx = tid + kT * i;
-      if (SCH % kT == 0 || idx < SCH) {
-        const int tensor = idx / (kStepRows * CPR), rem = idx % (kStepRows * CPR);
-        LdsTile<D>::store(stg[b][tensor], rem / CPR, rem % CPR, sreg[i]);
-      }
-    }
-    if (tid < kStepRows) {
-      meta[b].lse2[tid] = m_lse;
-      meta[b].dlt[tid] = m_dlt;
-      meta[b].lo[tid] = m_lo;
-      meta[b].hi[tid] = m_hi;
-    } else if (tid == kStepRows) {
-      meta[b].uni = m_uni;
-      meta[b].lo0 = m_lo;
-      meta[b].hi0 = m_hi;
-    }
-  };
-
-  auto step_hit = [&](int64_t st) -> bool {
-    if (st >= n_steps) return false;
-    const int64_t r0 = st * kStepRows;
-    const int64_t r1 = min(r0 + kStepRows, R) - 1;
-    const int b0 = static_cast<int>(r0 / grp / kBlock), b1 = static_cast<int>(r1 / grp / kBlock);
-    bool hit = false;
-    for (int b = b0; b <= b1; ++b) {
-      const int lo = self_tile ? kBlock * b : p.sample_start[b];
-      const int hi = self_tile ? kBlock * b + kBlock : p.anchor[b];
-      hit |= (lo <= kmax) && (hi > kmin);
-    }
-    return hit;
-  };
-
-  // Count the steps that reach this tile and split them over `parts` workgroups
-  // (interleaved), so that heavily read key tiles do not set the kernel's length.
-  int n_hit = 0;
-  for (int64_t base = 0; base < n_steps; base += kT) n_hit += __syncthreads_count(step_hit(base + tid));
-  const bool can_split = p.ws_parts != nullptr && !self_tile;
-  const int parts = can_split ? max(1, min(kMaxParts, (n_hit + kStepsPerPart - 1) / kStepsPerPart)) : 1;
-  if (part >= parts) return;
-  if (can_split && part == 0 && tid == 0) p.ws_parts[tile * p.hkv + g] = parts;
-
-  // V rows of the workgroup's keys -> LDS (row-major, chunk ^ (row & 7))
-  for (int idx = tid; idx < kKeysPerWG * CPR; idx += kT) {
-    const int row = idx / CPR, j = idx % CPR;
-    const int64_t src_row = min(krow0 + row, key_rows - 1);
-    LdsTile<D>::store(vtile, row, j, *reinterpret_cast<const u32x4*>(V + (src_row * p.hkv + g) * D + 8 * j));
-  }
-  bf16x8 kf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(K + (krc * p.hkv + g) * D + 16 * ks + 8 * h2));
-
-  int seen = 0;  // hits in earlier batches
-  for (int64_t base = 0; base < n_steps; base += kT) {
-    // compact this part's share of the batch's hits (global hit index % parts == part)
-    const bool hit = step_hit(base + tid);
-    const uint64_t mask = __ballot(hit);
-    if (lane == 0) wave_cnt[wave] = __popcll(mask);
-    __syncthreads();
-    int pre = 0, total_b = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) {
-      const int c = wave_cnt[w2];
-      pre += w2 < wave ? c : 0;
-      total_b += c;
-    }
-    const int gidx = seen + pre + __popcll(mask & ((uint64_t{1} << lane) - 1));
-    // entries of this part: gidx = part + parts * j  ->  list slot j - first_j
-    const int first_j = (seen - part + parts - 1) / parts;  // first j with part + parts*j >= seen
-    if (hit && (gidx - part) % parts == 0) step_list[(gidx - part) / parts - first_j] = static_cast<int>(base + tid);
-    const int last_excl = seen + total_b;  // hits [seen, last_excl) are in this batch
-    const int end_j = (last_excl - part + parts - 1) / parts;
-    const int total = max(0, end_j - first_j);
-    seen = last_excl;
-    __syncthreads();
-    if (total == 0) continue;
-
-    load_step(step_list[0]);
-    store_step(0);
-    __syncthreads();
-    int buf = 0;
-    for (int si = 0; si < total; ++si) {
-      const bool has_next = si + 1 < total;
-      if (has_next) load_step(step_list[si + 1]);
-
-      const StepMeta& mt = meta[buf];
-      // wave-uniform step facts in scalar registers
-      const bool uni = __builtin_amdgcn_readfirstlane(mt.uni) != 0;
-      const int lo0 = __builtin_amdgcn_readfirstlane(mt.lo0);
-      const int hi0 = __builtin_amdgcn_readfirstlane(mt.hi0);
-      const bool lane_ok = kvalid && kcoord >= lo0 && kcoord < hi0;
-      bool run = true, all_ok = false;
-      if (uni) {
-        run = __any(lane_ok);
-        all_ok = __all(lane_ok);
-      }
-      if (run) {
-        const uint16_t* lq = stg[buf][0];
-        const uint16_t* ld = stg[buf][1];
-        f32x16 sacc, pacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 qa = LdsTile<D>::frag(lq, l32, 2 * ks + h2);
-          const bf16x8 da = LdsTile<D>::frag(ld, l32, 2 * ks + h2);
-          const bf16x8 vb = LdsTile<D>::frag(vtile, krow, 2 * ks + h2);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, pacc, 0, 0, 0);
-        }
-        bf16x8 pb[2], sb[2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // rows 8j + 4h2 + 0..3 of the step
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&mt.lse2[8 * j + 4 * h2]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&mt.dlt[8 * j + 4 * h2]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * j + i;
-            float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], p.scale_log2, -l4[i]));
-            if (!all_ok) {
-              if (uni) {
-                pr = lane_ok ? pr : 0.f;
-              } else {
-                const int row = 8 * j + 4 * h2 + i;
-                if (!(kvalid && kcoord >= mt.lo[row] && kcoord < mt.hi[row])) pr = 0.f;
-              }
-            }
-            const float ds = pr * (pacc[r] - d4[i]);
-            pb[r / 8][r % 8] = static_cast<__bf16>(pr);
-            sb[r / 8][r % 8] = static_cast<__bf16>(ds);
-          }
-        }
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const int sl = lane & 15, col = 32 * dt + 16 * ((lane >> 4) & 1);
-            const bf16x8 dta = LdsTile<D>::frag_t(ld, tr_row_a(kq, h2, sl), tr_row_b(kq, h2, sl), col, sl);
-            const bf16x8 qta = LdsTile<D>::frag_t(lq, tr_row_a(kq, h2, sl), tr_row_b(kq, h2, sl), col, sl);
-            dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dta, pb[kq], dvacc[dt], 0, 0, 0);
-            dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, sb[kq], dkacc[dt], 0, 0, 0);
-          }
-        }
-      }
-
-      if (has_next) store_step(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
-  }
-
-  if (!kvalid) return;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int dcol = 32 * dt + 8 * jj + 4 * h2;
-      const f32x4 kv4 = f32x4{dkacc[dt][4 * jj], dkacc[dt][4 * jj + 1], dkacc[dt][4 * jj + 2], dkacc[dt][4 * jj + 3]};
-      const f32x4 vv4 = f32x4{dvacc[dt][4 * jj], dvacc[dt][4 * jj + 1], dvacc[dt][4 * jj + 2], dvacc[dt][4 * jj + 3]};
-      if (parts == 1) {
-        float* dK = self_tile ? p.dk_self : p.dk;
-        float* dV = self_tile ? p.dv_self : p.dv;
-        const int64_t o = (kr * p.hkv + g) * D + dcol;
-        *reinterpret_cast<f32x4*>(dK + o) = kv4 * p.scale;
-        *reinterpret_cast<f32x4*>(dV + o) = vv4;
-      } else {  // partial sums of this part: added up by the reduce pass
-        float* slot = p.ws_slots + ((static_cast<int64_t>(tile) * p.hkv + g) * kMaxParts + part) *
-                                       (static_cast<int64_t>(kKeysPerWG) * 2 * D);
-        *reinterpret_cast<f32x4*>(slot + (krow * 2 + 0) * D + dcol) = kv4;
-        *reinterpret_cast<f32x4*>(slot + (krow * 2 + 1) * D + dcol) = vv4;
-      }
-    }
 }
 
-// Sum of the partial dK/dV of split context tiles (one workgroup per tile and kv head).
+// In-place inclusive scan of prefix[1 .. n] (one workgroup of 1024 threads).
+__global__ __launch_bounds__(1024) void dkdv_scan_kernel(int32_t* prefix, int n) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int a = 1 + tid * per, e = min(n + 1, a + per);
+  int s = 0;
+  for (int i = a; i < e; ++i) s += prefix[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid > 0 ? part[tid - 1] : 0;
+  for (int i = a; i < e; ++i) {
+    run += prefix[i];
+    prefix[i] = run;
+  }
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p) {
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWaves))) void dkdv_bf16_kernel(
+    BwdParams p, DkdvSched sc) {
+  constexpr int H = kKvHalves;
+  constexpr int kT = 64 * kKvWaves;
+  constexpr int kWaves = kKvWaves;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int NI = 2 * kStepRows * CPR / kT;  // 16-byte copies per lane and step (Q, dO)
+  static_assert(NI >= 1 && NI * kT == 2 * kStepRows * CPR, "stage copy must split evenly over lanes");
+  constexpr int SE = 2 * kStepRows * D;  // elements of one stage: Q rows, then dO rows
+  __shared__ __attribute__((aligned(256))) uint16_t vtile[kKeysPerWG * D];
+  __shared__ __attribute__((aligned(256))) uint16_t stg[3][SE];
+  __shared__ __attribute__((aligned(16))) float smeta[3][2 * kStepRows];  // lse2 rows, delta rows
+  __shared__ int step_list[kListCap];
+  __shared__ int wave_cnt[kWaves];
+  __shared__ int red[2][kWaves];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
+  const int grp = p.hq / p.hkv;
+  const int n_q = p.n_blk * kBlock;
+  const StepGeo sg(grp, n_q);
+
+  // this workgroup's share of the (kv head, tile, hit step) list
+  const bool streamk = sc.n_shares > 0;
+  int share = blockIdx.x;
+  int64_t W = 0, pos = 0, end = 1;
+  if (streamk) {
+    if (sc.n_shares % 8 == 0) share = (blockIdx.x % 8) * (sc.n_shares / 8) + blockIdx.x / 8;  // XCD-local ranges
+    W = ld_uniform(sc.prefix, sc.n_tiles);
+    const int64_t tot = W * p.hkv;
+    pos = share * tot / sc.n_shares;
+    end = (share + 1) * tot / sc.n_shares;
+  }
+  const int64_t share_start = pos;
+
+  // element row (token * hq + head) of step row `row` relative to the step's start
+  auto row_elem = [&](int row, int g) {
+    const int r = min(row, (sg.hcs == 1 ? sg.ts * sg.gs : kStepRows) - 1);
+    return (r / sg.gs) * p.hq + g * grp + r % sg.gs;
+  };
+
+  while (pos < end) {
+    int g, t, s0, s1, hits = 0;
+    const int64_t seg_start = pos;
+    if (streamk) {
+      g = static_cast<int>(pos / W);
+      const int r = static_cast<int>(pos % W);
+      int lo = 0, hi = sc.n_tiles;  // prefix[lo] <= r < prefix[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (ld_uniform(sc.prefix, mid) <= r) lo = mid;
+        else hi = mid;
+      }
+      t = lo;
+      const int t0 = ld_uniform(sc.prefix, t), t1 = ld_uniform(sc.prefix, t + 1);
+      hits = t1 - t0;
+      s0 = r - t0;
+      s1 = static_cast<int>(min<int64_t>(t1, r + (end - pos)) - t0);
+      pos += s1 - s0;
+    } else {
+      g = blockIdx.x % p.hkv;
+      t = blockIdx.x / p.hkv;
+      s0 = 0;
+      s1 = 0x7fffffff;
+      pos = end;
+    }
+    const bool self_tile = t >= sc.n_ctx_tiles;
+    const int64_t key_rows = self_tile ? n_q : p.n_loc;
+    const int64_t krow0 = static_cast<int64_t>(self_tile ? t - sc.n_ctx_tiles : t) * kKeysPerWG;
+
+    // this lane's keys (columns of the two S tiles): local rows and key coordinates
+    int krow[H], kcoord[H];
+    bool kvalid[H];
+    int64_t krc[H];
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh) {
+      krow[hh] = kKeysPerWave * wave + 32 * hh + l32;
+      kvalid[hh] = krow0 + krow[hh] < key_rows;
+      krc[hh] = kvalid[hh] ? krow0 + krow[hh] : key_rows - 1;
+      kcoord[hh] = key_coord(p, self_tile, krc[hh]);
+    }
+    int kmin, kmax;
+    __syncthreads();  // the previous segment is done with vtile, red, the list and the stages
+    if (streamk) {
+      kmin = ld_uniform(sc.krange, 2 * t);
+      kmax = ld_uniform(sc.krange, 2 * t + 1);
+    } else {
+      kmin = 0x7fffffff;
+      kmax = -0x7fffffff;
+#pragma unroll
+      for (int hh = 0; hh < H; ++hh) {
+        kmin = min(kmin, kvalid[hh] ? kcoord[hh] : 0x7fffffff);
+        kmax = max(kmax, kvalid[hh] ? kcoord[hh] : -0x7fffffff);
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        kmin = min(kmin, __shfl_xor(kmin, off, 64));
+        kmax = max(kmax, __shfl_xor(kmax, off, 64));
+      }
+      if (lane == 0) {
+        red[0][wave] = kmin;
+        red[1][wave] = kmax;
+      }
+      __syncthreads();
+      kmin = red[0][0];
+      kmax = red[1][0];
+#pragma unroll
+      for (int w2 = 1; w2 < kWaves; ++w2) {
+        kmin = min(kmin, red[0][w2]);
+        kmax = max(kmax, red[1][w2]);
+      }
+    }
+
+    // V rows of the tile -> LDS; K of this wave's keys -> registers
+    {
+      const uint16_t* V = self_tile ? p.v_self : p.v;
+      for (int idx = tid; idx < kKeysPerWG * CPR; idx += kT) {
+        const int row = idx / CPR, j = idx % CPR;
+        const int64_t src_row = min(krow0 + row, key_rows - 1);
+        LdsTile<D>::store(vtile, row, j, *reinterpret_cast<const u32x4*>(V + (src_row * p.hkv + g) * D + 8 * j));
+      }
+    }
+    bf16x8 kf[H][KS];
+    {
+      const uint16_t* K = self_tile ? p.k_self : p.k;
+#pragma unroll
+      for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kf[hh][ks] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(K + (krc[hh] * p.hkv + g) * D + 16 * ks + 8 * h2));
+    }
+    wait_vmcnt<0>();  // the segment's own loads are complete before the copy pipeline starts
+    f32x16 dkacc[H][DT], dvacc[H][DT];
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dkacc[hh][dt][i] = dvacc[hh][dt][i] = 0.f;
+
+    // Copy sources: byte offset of each lane from the step's first element (rows
+    // past the step's used rows repeat its last row; all are masked)
+    int src_off[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int cc = ((wave * NI + j) * 64 + lane) % (kStepRows * CPR), row = cc / CPR;
+      const int logical = (cc % CPR) ^ LdsTile<D>::swz(row);
+      src_off[j] = 2 * (row_elem(row, g) * D + 8 * logical);
+    }
+    // wave 0, lanes 0..31: lse2 plane of row l32; lanes 32..63: delta plane
+    const int meta_off = 4 * row_elem(l32, g);
+    const int plane_off = h2 == 0 ? 4 * n_q * p.hq : 0;
+
+    // LDS byte offsets (see LdsTile): Q / dO row l32, V rows krow, transposed reads
+    int f_q = LdsTile<D>::frag_off(l32, h2);
+    int f_v = LdsTile<D>::frag_off(krow[0], h2);  // second half: + 32 rows
+    int t_a = LdsTile<D>::tr_off(4 * h2 + ((lane & 15) >> 2), (lane >> 4) & 1, lane & 15);
+    int t_b = LdsTile<D>::tr_off(8 + 4 * h2 + ((lane & 15) >> 2), (lane >> 4) & 1, lane & 15);
+    int rel = 4 * h2;  // step row of accumulator row 4 j + i: 8 j + rel + i
+
+    int scan = 0;  // next step to examine
+    int ord = 0;   // hits of this tile before `scan`
+    while (scan < sg.n_steps && ord < s1) {
+      // ---- collect the step indices of hits ord in [s0, s1), up to the list capacity
+      int cnt = 0;
+      while (scan < sg.n_steps && ord < s1 && cnt <= kListCap - kT) {
+        const int st = scan + tid;
+        const bool hit = step_hit(p, sg, st, n_q, self_tile, kmin, kmax);
+        const uint64_t m = __ballot(hit);
+        if (lane == 0) wave_cnt[wave] = __popcll(m);
+        __syncthreads();
+        int pre = 0, tot = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kWaves; ++w2) {
+          const int cw = wave_cnt[w2];
+          pre += w2 < wave ? cw : 0;
+          tot += cw;
+        }
+        const int o = ord + pre + __popcll(m & ((uint64_t{1} << lane) - 1));
+        const int first = max(ord, s0);
+        if (hit && o >= s0 && o < s1) step_list[cnt + o - first] = st;
+        cnt += max(0, min(ord + tot, s1) - first);
+        ord += tot;
+        scan += kT;
+        __syncthreads();
+      }
+
+      // ---- three-stage pipeline over the listed steps: iteration i waits for step
+      // i, copies step i + 2 into the stage step i - 1 used, then computes step i
+      for (int i = -2; i < cnt; ++i) {
+        if (i >= 0) {
+          if (i + 1 < cnt) {  // this wave's copies of step i landed; step i + 1 may fly
+            if (wave == 0) wait_vmcnt<NI + 1>();
+            else wait_vmcnt<NI>();
+          } else {
+            wait_vmcnt<0>();
+          }
+          barrier_nofence();  // every wave's copies landed; stage (i + 2) % 3 is free
+        }
+        if (i + 2 < cnt) {
+          const int nst = __builtin_amdgcn_readfirstlane(step_list[i + 2]);
+          const int sb2 = (i + 2) % 3;
+          const int64_t e0 = static_cast<int64_t>(sg.tok0(nst)) * p.hq + sg.h0(nst);  // first element row
+          // clamp to the arrays (rows past the end are masked)
+          const int lim_q = static_cast<int>(min<int64_t>(0x7fffffff, 2 * ((static_cast<int64_t>(n_q) * p.hq - e0) * D - 8)));
+          const int lim_m = static_cast<int>(4 * (static_cast<int64_t>(n_q) * p.hq - e0 - 1));
+#pragma unroll
+          for (int j = 0; j < NI; ++j) {
+            const bool is_do = (wave * NI + j) * 64 >= kStepRows * CPR;  // wave-uniform
+            dma16_s((is_do ? p.dout : p.q) + e0 * D, static_cast<uint32_t>(min(src_off[j], lim_q)),
+                    lds_addr(stg[sb2] + (wave * NI + j) * 512));
+          }
+          if (wave == 0)
+            dma4_s(p.delta + e0, static_cast<uint32_t>(min(meta_off, lim_m) + plane_off), lds_addr(&smeta[sb2][0]));
+        }
+        if (i < 0) continue;
+
+        // Per-lane constants are redefined opaquely every step so that the compiler
+        // recomputes the few values derived from them instead of holding dozens.
+        asm volatile("" : "+v"(f_q), "+v"(f_v), "+v"(t_a), "+v"(t_b), "+v"(rel));
+        const int sb = i % 3;
+        const int st = __builtin_amdgcn_readfirstlane(step_list[i]);
+        const int tk = sg.tok0(st);
+        const int rmax = sg.rows(st, n_q, grp);
+        const int b0 = tk / kBlock;
+        const int b1 = (tk + sg.ntok(st, n_q) - 1) / kBlock;
+        const int split = (kBlock * (b0 + 1) - tk) * sg.gs;  // rows < split are in block b0
+        const int lo0 = self_tile ? kBlock * b0 : ld_uniform(p.sample_start, b0);
+        const int hi0 = self_tile ? kBlock * b0 + kBlock : ld_uniform(p.anchor, b0);
+        const int lo1 = self_tile ? kBlock * b1 : ld_uniform(p.sample_start, b1);
+        const int hi1 = self_tile ? kBlock * b1 + kBlock : ld_uniform(p.anchor, b1);
+        bool ok0[H], ok1[H], any = false, all = true;
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh) {
+          ok0[hh] = kvalid[hh] && kcoord[hh] >= lo0 && kcoord[hh] < hi0;
+          ok1[hh] = kvalid[hh] && kcoord[hh] >= lo1 && kcoord[hh] < hi1;
+          any |= ok0[hh] || ok1[hh];
+          all &= ok0[hh] && ok1[hh];
+        }
+        if (!__any(any)) continue;
+        const bool all_ok = rmax == kStepRows && __all(all);
+        const uint16_t* lq = stg[sb];
+        const uint16_t* ld = stg[sb] + kStepRows * D;
+        f32x16 sacc[H], pacc[H];
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+          for (int i2 = 0; i2 < 16; ++i2) sacc[hh][i2] = pacc[hh][i2] = 0.f;
+        // operands are read one k-step ahead; the scheduling barriers keep the compiler
+        // from hoisting every k-step's reads (register pressure)
+        bf16x8 qa = LdsTile<D>::frag_at(lq, f_q), da = LdsTile<D>::frag_at(ld, f_q);
+        bf16x8 vb[H];
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh) vb[hh] = LdsTile<D>::frag_at(vtile + hh * 32 * D, f_v);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 cq = qa, cd = da;
+          bf16x8 cv[H];
+#pragma unroll
+          for (int hh = 0; hh < H; ++hh) cv[hh] = vb[hh];
+          if (ks + 1 < KS) {
+            const int o = f_q ^ (32 * (ks + 1)), ov = f_v ^ (32 * (ks + 1));
+            qa = LdsTile<D>::frag_at(lq, o);
+            da = LdsTile<D>::frag_at(ld, o);
+#pragma unroll
+            for (int hh = 0; hh < H; ++hh) vb[hh] = LdsTile<D>::frag_at(vtile + hh * 32 * D, ov);
+          }
+#pragma unroll
+          for (int hh = 0; hh < H; ++hh) {
+            sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cq, kf[hh][ks], sacc[hh], 0, 0, 0);
+            pacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cd, cv[hh], pacc[hh], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        u32x4 pw[H][2], sw[H][2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // rows 8 j + 4 h2 + 0..3 of the step
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&smeta[sb][8 * j + 4 * h2]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&smeta[sb][kStepRows + 8 * j + 4 * h2]);
+#pragma unroll
+          for (int hh = 0; hh < H; ++hh) {
+            float pr[4], ds[4];
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+              const int r = 4 * j + i2;
+              pr[i2] = __builtin_amdgcn_exp2f(fmaf(sacc[hh][r], p.scale_log2, -l4[i2]));
+              if (!all_ok) {  // row 8 j + rel + i2: compare rel with step-uniform bounds
+                const int c = 8 * j + i2;
+                const bool ok = (rel < split - c ? ok0[hh] : ok1[hh]) && rel < rmax - c;
+                pr[i2] = ok ? pr[i2] : 0.f;
+              }
+              ds[i2] = pr[i2] * (pacc[hh][r] - d4[i2]);
+            }
+            pw[hh][j / 2][2 * (j % 2)] = pack_bf16x2(pr[0], pr[1]);
+            pw[hh][j / 2][2 * (j % 2) + 1] = pack_bf16x2(pr[2], pr[3]);
+            sw[hh][j / 2][2 * (j % 2)] = pack_bf16x2(ds[0], ds[1]);
+            sw[hh][j / 2][2 * (j % 2) + 1] = pack_bf16x2(ds[2], ds[3]);
+          }
+        }
+        bf16x8 dta = LdsTile<D>::frag_t_at(ld, t_a, t_b), qta = LdsTile<D>::frag_t_at(lq, t_a, t_b);
+#pragma unroll
+        for (int kd = 0; kd < 2 * DT; ++kd) {
+          const int kq = kd / DT, dt = kd % DT;
+          const bf16x8 cdt = dta, cqt = qta;
+          if (kd + 1 < 2 * DT) {
+            const int kq1 = (kd + 1) / DT, dt1 = (kd + 1) % DT;
+            const int oa = (t_a ^ (64 * dt1)) + kq1 * 32 * D, ob = (t_b ^ (64 * dt1)) + kq1 * 32 * D;
+            dta = LdsTile<D>::frag_t_at(ld, oa, ob);
+            qta = LdsTile<D>::frag_t_at(lq, oa, ob);
+          }
+#pragma unroll
+          for (int hh = 0; hh < H; ++hh) {
+            dvacc[hh][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cdt, __builtin_bit_cast(bf16x8, pw[hh][kq]),
+                                                                    dvacc[hh][dt], 0, 0, 0);
+            dkacc[hh][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cqt, __builtin_bit_cast(bf16x8, sw[hh][kq]),
+                                                                    dkacc[hh][dt], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __syncthreads();  // all waves are done with the list and the stages
+    }
+
+    // ---- epilogue: whole tile -> dK, dV; partial -> this share's slot
+    const bool whole = !streamk || (s0 == 0 && s1 == hits);
+    float* slot = nullptr;
+    if (!whole)
+      slot = sc.slots + (2 * static_cast<int64_t>(share) + (seg_start == share_start ? 0 : 1)) *
+                            (static_cast<int64_t>(kKeysPerWG) * 2 * D);
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh) {
+      if (!kvalid[hh]) continue;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int dcol = 32 * dt + 8 * jj + 4 * h2;
+          const f32x4 kv4 = f32x4{dkacc[hh][dt][4 * jj], dkacc[hh][dt][4 * jj + 1], dkacc[hh][dt][4 * jj + 2],
+                                  dkacc[hh][dt][4 * jj + 3]};
+          const f32x4 vv4 = f32x4{dvacc[hh][dt][4 * jj], dvacc[hh][dt][4 * jj + 1], dvacc[hh][dt][4 * jj + 2],
+                                  dvacc[hh][dt][4 * jj + 3]};
+          if (whole) {
+            const int64_t o = ((krow0 + krow[hh]) * p.hkv + g) * D + dcol;
+            *reinterpret_cast<f32x4*>((self_tile ? p.dk_self : p.dk) + o) = kv4 * p.scale;
+            *reinterpret_cast<f32x4*>((self_tile ? p.dv_self : p.dv) + o) = vv4;
+          } else {
+            *reinterpret_cast<f32x4*>(slot + (krow[hh] * 2 + 0) * D + dcol) = kv4;
+            *reinterpret_cast<f32x4*>(slot + (krow[hh] * 2 + 1) * D + dcol) = vv4;
+          }
+        }
+    }
+  }
+}
+
+// Stream-K fix-up: one workgroup per (tile, kv head).  Tiles no step hits get
+// dK = dV = 0; tiles split over several shares get the sum of those shares' slots.
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, DkdvSched sc) {
   const int g = blockIdx.x % p.hkv;
-  const int tile = blockIdx.x / p.hkv;
-  const int parts = p.ws_parts[tile * p.hkv + g];
-  if (parts <= 1) return;
-  const int64_t slot_elems = static_cast<int64_t>(kKeysPerWG) * 2 * D;
-  const float* slots = p.ws_slots + (static_cast<int64_t>(tile) * p.hkv + g) * kMaxParts * slot_elems;
-  const int64_t krow0 = static_cast<int64_t>(tile) * kKeysPerWG;
+  const int t = blockIdx.x / p.hkv;
+  const bool self_tile = t >= sc.n_ctx_tiles;
+  const int64_t n_q = static_cast<int64_t>(p.n_blk) * kBlock;
+  const int64_t key_rows = self_tile ? n_q : p.n_loc;
+  const int64_t krow0 = static_cast<int64_t>(self_tile ? t - sc.n_ctx_tiles : t) * kKeysPerWG;
+  float* dK = self_tile ? p.dk_self : p.dk;
+  float* dV = self_tile ? p.dv_self : p.dv;
+  const int64_t W = sc.prefix[sc.n_tiles];
+  const int hits = sc.prefix[t + 1] - sc.prefix[t];
   constexpr int V4 = kKeysPerWG * 2 * D / 4;
+  if (hits == 0) {
+    for (int i = threadIdx.x; i < V4; i += 256) {
+      const int e = 4 * i;
+      const int krow = e / (2 * D), which = (e / D) % 2, dcol = e % D;
+      const int64_t kr = krow0 + krow;
+      if (kr >= key_rows) continue;
+      *reinterpret_cast<f32x4*>((which == 0 ? dK : dV) + (kr * p.hkv + g) * D + dcol) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  const int64_t tot = W * p.hkv, ns = sc.n_shares;
+  const int64_t G0 = static_cast<int64_t>(g) * W + sc.prefix[t], G1 = G0 + hits;
+  // share j covers [floor(j tot / ns), floor((j + 1) tot / ns)); share holding x:
+  const int64_t j0 = ((G0 + 1) * ns - 1) / tot, j1 = (G1 * ns - 1) / tot;
+  if (j0 == j1) return;  // one share covered the whole tile and wrote it
+  const bool j0_later = j0 * tot / ns < G0;  // the tile is not share j0's first segment
+  const int64_t slot_elems = static_cast<int64_t>(kKeysPerWG) * 2 * D;
   for (int i = threadIdx.x; i < V4; i += 256) {
     const int e = 4 * i;
     const int krow = e / (2 * D), which = (e / D) % 2, dcol = e % D;
     const int64_t kr = krow0 + krow;
-    if (kr >= p.n_loc) continue;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(slots + e);
-    for (int q = 1; q < parts; ++q) acc += *reinterpret_cast<const f32x4*>(slots + q * slot_elems + e);
-    float* dst = (which == 0 ? p.dk : p.dv) + (kr * p.hkv + g) * D + dcol;
-    *reinterpret_cast<f32x4*>(dst) = which == 0 ? acc * p.scale : acc;
+    if (kr >= key_rows) continue;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(sc.slots + (2 * j0 + (j0_later ? 1 : 0)) * slot_elems + e);
+    for (int64_t j = j0 + 1; j <= j1; ++j)
+      if ((j + 1) * tot / ns > j * tot / ns)  // empty shares (list shorter than the grid) wrote nothing
+        acc += *reinterpret_cast<const f32x4*>(sc.slots + 2 * j * slot_elems + e);
+    *reinterpret_cast<f32x4*>((which == 0 ? dK : dV) + (kr * p.hkv + g) * D + dcol) = which == 0 ? acc * p.scale : acc;
   }
+}
+
+int n_compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+struct WsLayout {
+  int64_t n_tiles, n_shares, prefix_off, krange_off, slots_off, bytes;
+};
+
+WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  WsLayout L;
+  L.n_tiles = (n_loc + kKeysPerWG - 1) / kKeysPerWG + (n_blk * kBlock + kKeysPerWG - 1) / kKeysPerWG;
+  L.n_shares = n_compute_units();
+  L.prefix_off = 0;
+  L.krange_off = up(4 * (L.n_tiles + 1));
+  L.slots_off = L.krange_off + up(8 * L.n_tiles);
+  L.bytes = L.slots_off + 2 * L.n_shares * static_cast<int64_t>(kKeysPerWG) * 2 * d * 4;
+  return L;
 }
 
 template <int D>
@@ -688,8 +931,6 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   p.dq_overwrite = (a.flags & SXA_BWD_DQ_OVERWRITE) != 0;
-  p.ws_parts = nullptr;
-  p.ws_slots = nullptr;
   if (a.flags & SXA_BWD_DQ) {
     const int64_t rows = static_cast<int64_t>(a.n_blk) * kBlock * (a.hq / a.hkv);
     const int64_t n_dq = (rows + 32 * kDqWaves - 1) / (32 * kDqWaves) * a.hkv;
@@ -702,29 +943,40 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   const int64_t n_self_tiles = a.k_self ? (n_q + kKeysPerWG - 1) / kKeysPerWG : 0;
   const int64_t n_tiles = n_ctx_tiles + n_self_tiles;
   if (n_tiles == 0) return hipSuccess;
-  const bool split = a.workspace != nullptr;
-  if (split) {
-    p.ws_parts = static_cast<int32_t*>(a.workspace);
-    p.ws_slots = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
-                                          ((n_ctx_tiles * a.hkv * 4 + 255) / 256) * 256);
+  DkdvSched sc;
+  sc.n_ctx_tiles = static_cast<int32_t>(n_ctx_tiles);
+  sc.n_tiles = static_cast<int32_t>(n_tiles);
+  sc.n_shares = 0;
+  sc.prefix = nullptr;
+  sc.krange = nullptr;
+  sc.slots = nullptr;
+  if (a.workspace != nullptr) {
+    const WsLayout L = ws_layout(a.n_blk, a.n_loc, D);
+    char* ws = static_cast<char*>(a.workspace);
+    int32_t* prefix = reinterpret_cast<int32_t*>(ws + L.prefix_off);
+    int32_t* krange = reinterpret_cast<int32_t*>(ws + L.krange_off);
+    sc.n_shares = static_cast<int32_t>(L.n_shares);
+    sc.prefix = prefix;
+    sc.krange = krange;
+    sc.slots = reinterpret_cast<float*>(ws + L.slots_off);
+    dkdv_count_kernel<<<dim3(static_cast<unsigned>(n_tiles)), dim3(256), 0, s>>>(p, sc, prefix, krange);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dkdv_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(prefix, static_cast<int>(n_tiles));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dkdv_bf16_kernel<D><<<dim3(static_cast<unsigned>(L.n_shares)), dim3(64 * kKvWaves), 0, s>>>(p, sc);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dkdv_reduce_kernel<D><<<dim3(static_cast<unsigned>(n_tiles * a.hkv)), dim3(256), 0, s>>>(p, sc);
+    return hipGetLastError();
   }
-  const int64_t n_kv = n_tiles * a.hkv * (split ? kMaxParts : 1);
-  dkdv_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_kv)), dim3(64 * kKvWaves), 0, s>>>(p, static_cast<int>(n_ctx_tiles),
-                                                                            static_cast<int>(n_tiles));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (split && n_ctx_tiles > 0) {
-    dkdv_reduce_kernel<D><<<dim3(static_cast<unsigned>(n_ctx_tiles * a.hkv)), dim3(256), 0, s>>>(p);
-    e = hipGetLastError();
-  }
-  return e;
+  dkdv_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_tiles * a.hkv)), dim3(64 * kKvWaves), 0, s>>>(p, sc);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-int64_t bwd_workspace_bytes(int64_t n_loc, int32_t hkv, int32_t d) {
-  const int64_t tiles = (n_loc + kKeysPerWG - 1) / kKeysPerWG;
-  return ((tiles * hkv * 4 + 255) / 256) * 256 +
-         tiles * hkv * kMaxParts * static_cast<int64_t>(kKeysPerWG) * 2 * d * 4;
+int64_t bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hkv, int32_t d) {
+  (void)hkv;
+  return ws_layout(n_blk, n_loc, d).bytes;
 }
 
 hipError_t launch_bwd_bf16(const AttnArgs& a, hipStream_t s) {

@@ -110,10 +110,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(AttnArgs a) {
   if (cg == 0) a.lse[orow] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
-// delta[row] = sum_d dout[row][d] * o[row][d]; 16 lanes per row.
+// delta[row] = sum_d dout[row][d] * o[row][d], and delta[rows + row] = lse[row] in
+// log2 units (the per-row inputs of the bf16 backward); 16 lanes per row.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void delta_kernel(const T* __restrict__ o,
                                                          const T* __restrict__ dout,
+                                                         const float* __restrict__ lse,
                                                          float* __restrict__ delta, int64_t rows) {
   constexpr int EPL = D / 16;
   const int lane = threadIdx.x % 16;
@@ -127,7 +129,12 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const T* __restrict__ o
   }
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 16);
-  if (lane == 0 && r_raw < rows) delta[r] = s;
+  if (lane == 0 && r_raw < rows) {
+    delta[r] = s;
+    // second plane: lse in log2 units, +inf for rows without any key (exp2(x - inf) = 0)
+    const float l = lse[r];
+    delta[rows + r] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
 }
 
 // Query-major backward: dq_accum[i][h] += scale * sum_j dS_ij K_j over this call's keys.
@@ -358,13 +365,13 @@ hipError_t launch_delta(const AttnArgs& a, bool bf16, hipStream_t s) {
   if (bf16) {
     const uint16_t* o = static_cast<const uint16_t*>(a.o_in);
     const uint16_t* d = static_cast<const uint16_t*>(a.dout);
-    if (a.d == 64) delta_kernel<uint16_t, 64><<<grid, kThreads, 0, s>>>(o, d, a.delta, rows);
-    else delta_kernel<uint16_t, 128><<<grid, kThreads, 0, s>>>(o, d, a.delta, rows);
+    if (a.d == 64) delta_kernel<uint16_t, 64><<<grid, kThreads, 0, s>>>(o, d, a.lse_in, a.delta, rows);
+    else delta_kernel<uint16_t, 128><<<grid, kThreads, 0, s>>>(o, d, a.lse_in, a.delta, rows);
   } else {
     const float* o = static_cast<const float*>(a.o_in);
     const float* d = static_cast<const float*>(a.dout);
-    if (a.d == 64) delta_kernel<float, 64><<<grid, kThreads, 0, s>>>(o, d, a.delta, rows);
-    else delta_kernel<float, 128><<<grid, kThreads, 0, s>>>(o, d, a.delta, rows);
+    if (a.d == 64) delta_kernel<float, 64><<<grid, kThreads, 0, s>>>(o, d, a.lse_in, a.delta, rows);
+    else delta_kernel<float, 128><<<grid, kThreads, 0, s>>>(o, d, a.lse_in, a.delta, rows);
   }
   return hipGetLastError();
 }

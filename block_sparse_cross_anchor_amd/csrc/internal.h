@@ -44,7 +44,7 @@ struct AttnArgs {
 };
 
 // Bytes of dK/dV split scratch for n_loc local rows (0 if not representable).
-int64_t bwd_workspace_bytes(int64_t n_loc, int32_t hkv, int32_t d);
+int64_t bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hkv, int32_t d);
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t s);

@@ -57,6 +57,29 @@ struct LdsTile {
     const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
     return __builtin_bit_cast(bf16x8, u32x4{ua[0], ua[1], ub[0], ub[1]});
   }
+
+  // Offset form for loops over k-steps, on tiles whose base is 256-byte aligned.  A
+  // row is 2 D bytes and the swizzle only permutes the 16-byte chunk bits inside it,
+  // so the step-dependent part of an address is a constant XOR:
+  //   frag(row, 2 ks + h)        at byte  frag_off(row, h) ^ (32 ks)
+  //   frag_t(rows of k-step kq, col = 32 dt + 16 hb)
+  //                              at bytes tr_off(r, hb, s) ^ (64 dt) + kq 16 rows,
+  //                              r = 4 h + s / 4 (first read) or 8 + 4 h + s / 4.
+  __device__ static __forceinline__ int frag_off(int row, int h) { return row * 2 * D + 16 * (h ^ swz(row)); }
+  __device__ static __forceinline__ int tr_off(int row, int hb, int s) {
+    const int lowc = 2 * hb + ((s & 3) >> 1);  // chunk bits below the column-block bits
+    return row * 2 * D + 16 * (lowc ^ swz(row)) + 8 * (s & 1);
+  }
+  __device__ static __forceinline__ bf16x8 frag_at(const uint16_t* base, int byte_off) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off));
+  }
+  __device__ static __forceinline__ bf16x8 frag_t_at(const uint16_t* base, int off_a, int off_b) {
+    const char* b8 = reinterpret_cast<const char*>(base);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b8 + off_a));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b8 + off_b));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return __builtin_bit_cast(bf16x8, u32x4{ua[0], ua[1], ub[0], ub[1]});
+  }
 };
 
 // Key order shared by P (or dS) held in MFMA accumulator registers and the
@@ -82,6 +105,55 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(gptr), "s"(base)
+      : "memory");
+}
+
+// 4-byte variant (global_load_lds_dword): lane i writes LDS bytes [lds_base + 4 i, +4).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(base)
+      : "memory");
+}
+
+// Scalar-base forms: the wave-uniform 64-bit base sits in SGPRs and each lane adds a
+// 32-bit byte offset (one VGPR per copy instead of a 64-bit address).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(uniform_ptr(sbase)), "s"(base)
+      : "memory");
+}
+
+__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(uniform_ptr(sbase)), "s"(base)
       : "memory");
 }
 

@@ -50,7 +50,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_xattn_fwd.argtypes = attn_common + [P, ctypes.c_int, P, P]
     lib.sparse_xattn_fwd.restype = ctypes.c_int
     lib.sparse_xattn_bwd.argtypes = attn_common + [P, P, P, P, P, P, P, P, P, P, I64, I32, P]
-    lib.sparse_xattn_bwd_workspace_bytes.argtypes = [I64, I32, I32]
+    lib.sparse_xattn_bwd_workspace_bytes.argtypes = [I32, I64, I32, I32]
     lib.sparse_xattn_bwd_workspace_bytes.restype = I64
     lib.sparse_xattn_bwd.restype = ctypes.c_int
     lib.lse_combine.argtypes = [P, ctypes.c_int, P, I32, I64, I32, P, ctypes.c_int, P, P]
@@ -150,10 +150,12 @@ def sparse_xattn_fwd(q, k, v, meta: Meta, scale: float, k_self=None, v_self=None
 _workspaces = {}
 
 
-def bwd_workspace(n_loc: int, hkv: int, d: int, device) -> torch.Tensor:
-    """Scratch that lets the dK/dV phase split heavily read key tiles (cached per device;
-    grown on demand)."""
-    need = int(load_library().sparse_xattn_bwd_workspace_bytes(int(n_loc), int(hkv), int(d)))
+def bwd_workspace(n_blk: int, n_loc: int, hkv: int, d: int, device) -> torch.Tensor:
+    """Scratch of the load-balanced dK/dV phase (cached per device; grown on demand).
+    Calls that share it must be ordered on one stream."""
+    with torch.cuda.device(torch.device(device)):
+        need = int(load_library().sparse_xattn_bwd_workspace_bytes(int(n_blk), int(n_loc), int(hkv),
+                                                                    int(d)))
     key = torch.device(device)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
@@ -178,7 +180,8 @@ def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
     _need(lse, "lse", (n_q, hq), torch.float32)
     _need(dq_accum, "dq_accum", (n_q, hq, d), torch.float32)
     if delta_ws is None:
-        delta_ws = torch.empty((n_q, hq), dtype=torch.float32, device=q.device)
+        delta_ws = torch.empty((2, n_q, hq), dtype=torch.float32, device=q.device)
+    _need(delta_ws, "delta_ws", (2, n_q, hq), torch.float32)
     f32 = torch.float32
     if dk is None:
         dk = torch.empty(k.shape, dtype=f32, device=k.device)
@@ -197,7 +200,7 @@ def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
         _need(dv_self, "dv_self", v_self.shape, f32)
     lib = load_library()
     if isinstance(workspace, str):  # "auto"
-        workspace = bwd_workspace(meta.n_loc, hkv, d, q.device)
+        workspace = bwd_workspace(meta.n_blk, meta.n_loc, hkv, d, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.sparse_xattn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), meta.n_blk, BLOCK, hq, hkv, d, float(scale),

@@ -24,7 +24,8 @@
  *   k, v, dk, dv          : [n_loc][hkv][d]   local rows = the listed chunks back to back
  *   k_self, v_self, dk_self, dv_self : [n_q][hkv][d]  keys/values of the draft tokens
  *   (gradients dq_accum, dk, dv, dk_self, dv_self are always float32)
- *   lse, delta_ws         : [n_q][hq] float32
+ *   lse                   : [n_q][hq] float32
+ *   delta_ws              : [2][n_q][hq] float32
  * Query head h reads kv head h / (hq / hkv).
  * Metadata (device int32 arrays):
  *   anchor[b], sample_start[b]  global packed positions of block b's anchor and of
@@ -91,7 +92,7 @@ int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_d
 
 /* Phases of sparse_xattn_bwd (bit flags; 0 means all of DELTA | DQ | DKDV). */
 enum {
-  SXA_BWD_DELTA = 1,         /* pre-pass: delta_ws = rowsum(dout * o) */
+  SXA_BWD_DELTA = 1,         /* pre-pass: delta_ws = (rowsum(dout * o), lse * log2 e) */
   SXA_BWD_DQ = 2,            /* add this call's query gradient to dq_accum */
   SXA_BWD_DKDV = 4,          /* write dk, dv (and dk_self, dv_self) */
   SXA_BWD_DQ_OVERWRITE = 8   /* with SXA_BWD_DQ: overwrite dq_accum instead of adding */
@@ -102,19 +103,22 @@ enum {
  * merged output o, merged lse and upstream gradient dout (all [n_q][hq], dtype
  * in_dtype for o/dout).  Keys/values stay local: the gradient of the local rows is
  * produced here ("Exchange the smaller side": local in forward and backward).
- *   delta_ws [n_q][hq] float32: written by the SXA_BWD_DELTA phase, read by the
- *            others (a caller that already holds rowsum(dout * o) from an earlier
- *            call with the same o and dout may skip the phase).
+ *   delta_ws [2][n_q][hq] float32: written by the SXA_BWD_DELTA phase, read by the
+ *            others: plane 0 holds rowsum(dout * o), plane 1 lse * log2(e) (+inf
+ *            where lse = -inf).  A caller that already holds it from an earlier call
+ *            with the same o, dout and lse may skip the phase.
  *   dq_accum [n_q][hq][d] float32: this call's query gradient is ADDED to it (or
  *            written, with SXA_BWD_DQ_OVERWRITE), so per-chunk calls accumulate.
  *   dk, dv   [n_loc][hkv][d] float32: overwritten.
  *   dk_self, dv_self [n_q][hkv][d] float32: overwritten when k_self != NULL
  *            (must then be non-NULL), ignored otherwise.
  *   workspace, workspace_bytes: optional device scratch for the bf16 dK/dV phase.
- *            With at least sparse_xattn_bwd_workspace_bytes() bytes, key tiles that
- *            many query blocks read are split over up to four workgroups whose
- *            partial sums are added by a second pass; with NULL (or too small) every
- *            key tile is handled by one workgroup.  Contents are scratch.
+ *            With at least sparse_xattn_bwd_workspace_bytes() bytes the phase is
+ *            load-balanced: one workgroup per compute unit, each taking an equal
+ *            share of all (key tile, query step) work, with the partial sums of
+ *            tiles split between workgroups added by a second pass.  With NULL (or
+ *            too small) every 256-key tile is handled by one workgroup.  Contents
+ *            are scratch; calls that share a workspace must be ordered on one stream.
  *   flags    SXA_BWD_* bits selecting the phases; they run in the order
  *            DELTA, DQ, DKDV on `stream`.
  */
@@ -128,9 +132,10 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                      void* dk_self, void* dv_self, void* workspace, int64_t workspace_bytes,
                      int32_t flags, void* stream);
 
-/* Workspace bytes that let sparse_xattn_bwd split heavily read key tiles
- * (a function of n_loc, hkv and d only; 0 for invalid sizes). */
-int64_t sparse_xattn_bwd_workspace_bytes(int64_t n_loc, int32_t hkv, int32_t d);
+/* Workspace bytes for the load-balanced dK/dV phase of sparse_xattn_bwd on the
+ * current device (a function of n_blk, n_loc, d and the device's compute-unit count;
+ * 0 for invalid sizes). */
+int64_t sparse_xattn_bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hkv, int32_t d);
 
 /*
  * Exact merge of n_parts partials from their log-sum-exp statistics
