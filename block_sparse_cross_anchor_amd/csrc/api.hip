@@ -98,7 +98,8 @@ int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                      float scale, const int32_t* anchor, const int32_t* sample_start,
                      const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
                      int64_t n_loc, const void* k_self, const void* v_self, void* o,
-                     sxa_dtype o_dtype, float* lse, void* stream) {
+                     sxa_dtype o_dtype, float* lse, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
   sxa::AttnArgs a;
   int st = check_attn(q, k, v, in_dtype, n_blk, block_size, hq, hkv, d, scale, anchor,
                       sample_start, chunk_gstart, chunk_len, n_chunk, n_loc, k_self, v_self, a);
@@ -110,6 +111,9 @@ int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_d
   a.o = o;
   a.o_bf16 = o_dtype == SXA_BF16;
   a.lse = lse;
+  if (workspace_bytes < 0) return fail(SXA_EINVAL, "workspace_bytes must be >= 0");
+  const int64_t need = sparse_xattn_fwd_workspace_bytes(n_blk, hq, hkv);
+  if (workspace != nullptr && need > 0 && workspace_bytes >= need) a.rg_order = static_cast<int32_t*>(workspace);
   if (n_blk == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(in_dtype == SXA_BF16 ? sxa::launch_fwd_bf16(a, s) : sxa::launch_fwd_f32(a, s),
@@ -150,7 +154,7 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
   a.dv_self = dv_self;
   a.flags = flags;
   if (workspace_bytes < 0) return fail(SXA_EINVAL, "workspace_bytes must be >= 0");
-  const int64_t need = sxa::bwd_workspace_bytes(n_blk, n_loc, hkv, d);
+  const int64_t need = sxa::bwd_workspace_bytes(n_blk, n_loc, hq, hkv, d);
   a.workspace = (workspace != nullptr && need > 0 && workspace_bytes >= need) ? workspace : nullptr;
   a.workspace_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -166,9 +170,20 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                     "sparse_xattn_bwd launch");
 }
 
-int64_t sparse_xattn_bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hkv, int32_t d) {
-  if (n_blk < 0 || n_loc < 0 || hkv <= 0 || (d != 64 && d != 128)) return 0;
-  return sxa::bwd_workspace_bytes(n_blk, n_loc, hkv, d);
+int64_t sparse_xattn_fwd_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv) {
+  if (n_blk < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return 0;
+  sxa::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.n_blk = n_blk;
+  a.hq = hq;
+  a.hkv = hkv;
+  const int64_t groups = sxa::row_groups(a, sxa::kRowsPerGroup);
+  return 4 * (groups < sxa::kMaxOrderedGroups ? groups : sxa::kMaxOrderedGroups);
+}
+
+int64_t sparse_xattn_bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hq, int32_t hkv, int32_t d) {
+  if (n_blk < 0 || n_loc < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || (d != 64 && d != 128)) return 0;
+  return sxa::bwd_workspace_bytes(n_blk, n_loc, hq, hkv, d);
 }
 
 int lse_combine(const void* o_parts, sxa_dtype part_dtype, const float* lse_parts,

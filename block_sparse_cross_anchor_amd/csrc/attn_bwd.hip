@@ -61,6 +61,7 @@ struct BwdParams {
   float scale;
   float scale_log2;  // scale * log2(e)
   int32_t dq_overwrite;
+  const int32_t* rg_order;  // dQ: row group of workgroup blockIdx / hkv (nullptr: identity)
 };
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
@@ -179,7 +180,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
   const int g = blockIdx.x % p.hkv;
-  const int wg = blockIdx.x / p.hkv;
+  const int wg = p.rg_order ? p.rg_order[blockIdx.x / p.hkv] : static_cast<int>(blockIdx.x / p.hkv);
   const int grp = p.hq / p.hkv;
   const int64_t R = static_cast<int64_t>(p.n_blk) * kBlock * grp;
   const int64_t wg_row0 = static_cast<int64_t>(wg) * ROWS;
@@ -884,17 +885,19 @@ int n_compute_units() {
 }
 
 struct WsLayout {
-  int64_t n_tiles, n_shares, prefix_off, krange_off, slots_off, bytes;
+  int64_t n_tiles, n_shares, prefix_off, krange_off, order_off, slots_off, bytes;
 };
 
-WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d) {
+WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d, int64_t grp) {
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   WsLayout L;
   L.n_tiles = (n_loc + kKeysPerWG - 1) / kKeysPerWG + (n_blk * kBlock + kKeysPerWG - 1) / kKeysPerWG;
   L.n_shares = n_compute_units();
+  const int64_t groups = (n_blk * kBlock * grp + kRowsPerGroup - 1) / kRowsPerGroup;
   L.prefix_off = 0;
   L.krange_off = up(4 * (L.n_tiles + 1));
-  L.slots_off = L.krange_off + up(8 * L.n_tiles);
+  L.order_off = L.krange_off + up(8 * L.n_tiles);
+  L.slots_off = L.order_off + up(4 * (groups < kMaxOrderedGroups ? groups : int64_t{kMaxOrderedGroups}));
   L.bytes = L.slots_off + 2 * L.n_shares * static_cast<int64_t>(kKeysPerWG) * 2 * d * 4;
   return L;
 }
@@ -931,9 +934,17 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   p.dq_overwrite = (a.flags & SXA_BWD_DQ_OVERWRITE) != 0;
+  p.rg_order = nullptr;
   if (a.flags & SXA_BWD_DQ) {
-    const int64_t rows = static_cast<int64_t>(a.n_blk) * kBlock * (a.hq / a.hkv);
-    const int64_t n_dq = (rows + 32 * kDqWaves - 1) / (32 * kDqWaves) * a.hkv;
+    static_assert(32 * kDqWaves == kRowsPerGroup, "row groups are shared with the dispatch order");
+    const int64_t groups = row_groups(a, kRowsPerGroup);
+    const int64_t n_dq = groups * a.hkv;
+    if (a.workspace != nullptr && groups <= kMaxOrderedGroups) {
+      const WsLayout L = ws_layout(a.n_blk, a.n_loc, D, a.hq / a.hkv);
+      int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + L.order_off);
+      if ((e = launch_row_group_order(a, kRowsPerGroup, order, s)) != hipSuccess) return e;
+      p.rg_order = order;
+    }
     dq_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_dq)), dim3(64 * kDqWaves), 0, s>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -951,7 +962,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   sc.krange = nullptr;
   sc.slots = nullptr;
   if (a.workspace != nullptr) {
-    const WsLayout L = ws_layout(a.n_blk, a.n_loc, D);
+    const WsLayout L = ws_layout(a.n_blk, a.n_loc, D, a.hq / a.hkv);
     char* ws = static_cast<char*>(a.workspace);
     int32_t* prefix = reinterpret_cast<int32_t*>(ws + L.prefix_off);
     int32_t* krange = reinterpret_cast<int32_t*>(ws + L.krange_off);
@@ -974,9 +985,8 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int64_t bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hkv, int32_t d) {
-  (void)hkv;
-  return ws_layout(n_blk, n_loc, d).bytes;
+int64_t bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hq, int32_t hkv, int32_t d) {
+  return ws_layout(n_blk, n_loc, d, hq / hkv).bytes;
 }
 
 hipError_t launch_bwd_bf16(const AttnArgs& a, hipStream_t s) {

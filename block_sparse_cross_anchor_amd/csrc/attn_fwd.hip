@@ -59,6 +59,7 @@ struct FwdParams {
   const int32_t* chunk_len;
   void* o;
   float* lse;
+  const int32_t* rg_order;  // row group of workgroup blockIdx / hkv (nullptr: identity)
   int32_t n_blk, hq, hkv, n_chunk;
   float scale_log2;  // scale * log2(e)
 };
@@ -169,7 +170,7 @@ fwd_bf16_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
   const int g = blockIdx.x % p.hkv;
-  const int wg = blockIdx.x / p.hkv;
+  const int wg = p.rg_order ? p.rg_order[blockIdx.x / p.hkv] : static_cast<int>(blockIdx.x / p.hkv);
   const int grp = p.hq / p.hkv;
   const int64_t R = static_cast<int64_t>(p.n_blk) * kBlock * grp;
   const int64_t wg_row0 = static_cast<int64_t>(wg) * ROWS;
@@ -415,6 +416,7 @@ fwd_bf16_kernel(FwdParams p) {
 constexpr int kNT = 1;                  // 32 query rows per wave
 constexpr int kWaves = SXA_FWD_WAVES;   // waves sharing each K/V tile
 constexpr int kRowsPerWG = 32 * kNT * kWaves;
+static_assert(kRowsPerWG == kRowsPerGroup, "row groups are shared with the dispatch order");
 
 template <int D, bool OUT_BF16>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
@@ -430,6 +432,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   p.chunk_len = a.chunk_len;
   p.o = a.o;
   p.lse = a.lse;
+  p.rg_order = a.rg_order;
   p.n_blk = a.n_blk;
   p.hq = a.hq;
   p.hkv = a.hkv;
@@ -439,6 +442,14 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   const int64_t groups = (rows + kRowsPerWG - 1) / kRowsPerWG;
   const int64_t n_wg = groups * a.hkv;
   if (n_wg == 0) return hipSuccess;
+  if (p.rg_order != nullptr) {
+    if (groups > kMaxOrderedGroups) {
+      p.rg_order = nullptr;
+    } else {
+      const hipError_t e = launch_row_group_order(a, kRowsPerWG, a.rg_order, s);
+      if (e != hipSuccess) return e;
+    }
+  }
   fwd_bf16_kernel<D, kNT, kWaves, OUT_BF16>
       <<<dim3(static_cast<unsigned>(n_wg)), dim3(64 * kWaves), 0, s>>>(p);
   return hipGetLastError();

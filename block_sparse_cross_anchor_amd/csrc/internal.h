@@ -41,10 +41,20 @@ struct AttnArgs {
   int32_t flags;  // SXA_BWD_* phases (never 0 here)
   void* workspace;  // optional dK/dV split scratch (nullptr: no split)
   int64_t workspace_bytes;
+  int32_t* rg_order;  // optional scratch for the row-group dispatch order (nullptr: index order)
 };
 
+// Query rows per forward / dQ workgroup, and the largest row-group count that is
+// dispatched in cost order (beyond it: index order).
+constexpr int kRowsPerGroup = 256;
+constexpr int kMaxOrderedGroups = 4096;
+int64_t row_groups(const AttnArgs& a, int rows_per_group);
+// Write the row groups of `a` into order[0 .. n), most 64-key tiles first (no-op
+// when there are more than kMaxOrderedGroups groups).
+hipError_t launch_row_group_order(const AttnArgs& a, int rows_per_group, int32_t* order, hipStream_t s);
+
 // Bytes of dK/dV split scratch for n_loc local rows (0 if not representable).
-int64_t bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hkv, int32_t d);
+int64_t bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hq, int32_t hkv, int32_t d);
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t s);

@@ -22,7 +22,8 @@ SXA_OK, SXA_EINVAL, SXA_EUNSUPPORTED, SXA_EHIP = 0, -1, -2, -3
 BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_DQ_OVERWRITE = 1, 2, 4, 8
 BLOCK = 16
 
-EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_bwd", "sparse_xattn_bwd_workspace_bytes",
+EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_fwd_workspace_bytes", "sparse_xattn_bwd",
+           "sparse_xattn_bwd_workspace_bytes",
            "lse_combine", "chunk_cost", "lpt_assign", "context_gather", "sxa_last_error")
 
 _lib = None
@@ -47,10 +48,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     attn_common = [P, P, P, ctypes.c_int, I32, I32, I32, I32, I32, F32, P, P, P, P, I32, I64, P, P]
-    lib.sparse_xattn_fwd.argtypes = attn_common + [P, ctypes.c_int, P, P]
+    lib.sparse_xattn_fwd.argtypes = attn_common + [P, ctypes.c_int, P, P, I64, P]
     lib.sparse_xattn_fwd.restype = ctypes.c_int
+    lib.sparse_xattn_fwd_workspace_bytes.argtypes = [I32, I32, I32]
+    lib.sparse_xattn_fwd_workspace_bytes.restype = I64
     lib.sparse_xattn_bwd.argtypes = attn_common + [P, P, P, P, P, P, P, P, P, P, I64, I32, P]
-    lib.sparse_xattn_bwd_workspace_bytes.argtypes = [I32, I64, I32, I32]
+    lib.sparse_xattn_bwd_workspace_bytes.argtypes = [I32, I64, I32, I32, I32]
     lib.sparse_xattn_bwd_workspace_bytes.restype = I64
     lib.sparse_xattn_bwd.restype = ctypes.c_int
     lib.lse_combine.argtypes = [P, ctypes.c_int, P, I32, I64, I32, P, ctypes.c_int, P, P]
@@ -119,8 +122,9 @@ class Meta:
 
 
 def sparse_xattn_fwd(q, k, v, meta: Meta, scale: float, k_self=None, v_self=None,
-                     out_dtype=None, out=None, lse=None):
-    """Partial forward over the local chunks (+ own-block term).  Returns (o, lse)."""
+                     out_dtype=None, out=None, lse=None, workspace="auto"):
+    """Partial forward over the local chunks (+ own-block term).  Returns (o, lse).
+    ``workspace``: "auto" (cached scratch), None, or a device tensor."""
     n_q, hq, d = q.shape
     hkv = k.shape[1]
     _need(q, "q", dtype=q.dtype)
@@ -139,29 +143,38 @@ def sparse_xattn_fwd(q, k, v, meta: Meta, scale: float, k_self=None, v_self=None
     _need(out, "out", (n_q, hq, d), out_dtype)
     _need(lse, "lse", (n_q, hq), torch.float32)
     lib = load_library()
+    if isinstance(workspace, str):  # "auto"
+        workspace = _scratch("fwd", int(lib.sparse_xattn_fwd_workspace_bytes(meta.n_blk, hq, hkv)),
+                             q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.sparse_xattn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), meta.n_blk, BLOCK, hq, hkv, d, float(scale),
         _ptr(meta.anchor), _ptr(meta.sample_start), _ptr(meta.chunk_gstart), _ptr(meta.chunk_len),
         meta.n_chunk, meta.n_loc, _ptr(k_self), _ptr(v_self), _ptr(out), _dtype_code(out),
-        _ptr(lse), _stream()))
+        _ptr(lse), _ptr(workspace), ws_bytes, _stream()))
     return out, lse
 
 
 _workspaces = {}
 
 
-def bwd_workspace(n_blk: int, n_loc: int, hkv: int, d: int, device) -> torch.Tensor:
-    """Scratch of the load-balanced dK/dV phase (cached per device; grown on demand).
-    Calls that share it must be ordered on one stream."""
-    with torch.cuda.device(torch.device(device)):
-        need = int(load_library().sparse_xattn_bwd_workspace_bytes(int(n_blk), int(n_loc), int(hkv),
-                                                                    int(d)))
-    key = torch.device(device)
+def _scratch(kind: str, need: int, device) -> torch.Tensor:
+    """Cached device scratch per (kind, device), grown on demand.  Calls that share
+    it must be ordered on one stream."""
+    key = (kind, torch.device(device))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=key)
+        ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=key[1])
         _workspaces[key] = ws
     return ws
+
+
+def bwd_workspace(n_blk: int, n_loc: int, hq: int, hkv: int, d: int, device) -> torch.Tensor:
+    """Scratch of the load-balanced dQ and dK/dV phases (cached per device)."""
+    with torch.cuda.device(torch.device(device)):
+        need = int(load_library().sparse_xattn_bwd_workspace_bytes(int(n_blk), int(n_loc), int(hq),
+                                                                    int(hkv), int(d)))
+    return _scratch("bwd", need, device)
 
 
 def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
@@ -200,7 +213,7 @@ def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
         _need(dv_self, "dv_self", v_self.shape, f32)
     lib = load_library()
     if isinstance(workspace, str):  # "auto"
-        workspace = bwd_workspace(meta.n_blk, meta.n_loc, hkv, d, q.device)
+        workspace = bwd_workspace(meta.n_blk, meta.n_loc, hq, hkv, d, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.sparse_xattn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), meta.n_blk, BLOCK, hq, hkv, d, float(scale),

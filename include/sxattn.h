@@ -80,6 +80,11 @@ typedef enum {
  *   hq % hkv == 0.  n_chunk >= 0 (0 with k_self set gives the own-block partial alone).
  *   o [n_q][hq][d] in o_dtype (SXA_F32 or SXA_BF16; SXA_F32 input requires SXA_F32 output),
  *   lse [n_q][hq] float32.  Both are overwritten.
+ *   workspace, workspace_bytes: optional device scratch (at least
+ *   sparse_xattn_fwd_workspace_bytes() bytes, else ignored).  With it the bf16 path
+ *   first ranks its query row groups by the number of key tiles they read and
+ *   dispatches the heaviest first; results do not depend on it.  Calls that share a
+ *   workspace must be ordered on one stream.
  * bf16 inputs run on bf16 MFMA with float32 accumulation and statistics; float32
  * inputs run in float32 throughout.
  */
@@ -88,7 +93,11 @@ int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                      float scale, const int32_t* anchor, const int32_t* sample_start,
                      const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
                      int64_t n_loc, const void* k_self, const void* v_self,
-                     void* o, sxa_dtype o_dtype, float* lse, void* stream);
+                     void* o, sxa_dtype o_dtype, float* lse, void* workspace,
+                     int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes of sparse_xattn_fwd's load balancing (0 for invalid sizes). */
+int64_t sparse_xattn_fwd_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv);
 
 /* Phases of sparse_xattn_bwd (bit flags; 0 means all of DELTA | DQ | DKDV). */
 enum {
@@ -132,10 +141,11 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                      void* dk_self, void* dv_self, void* workspace, int64_t workspace_bytes,
                      int32_t flags, void* stream);
 
-/* Workspace bytes for the load-balanced dK/dV phase of sparse_xattn_bwd on the
- * current device (a function of n_blk, n_loc, d and the device's compute-unit count;
+/* Workspace bytes for the load-balanced dQ and dK/dV phases of sparse_xattn_bwd on
+ * the current device (a function of the sizes and the device's compute-unit count;
  * 0 for invalid sizes). */
-int64_t sparse_xattn_bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hkv, int32_t d);
+int64_t sparse_xattn_bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hq, int32_t hkv,
+                                         int32_t d);
 
 /*
  * Exact merge of n_parts partials from their log-sum-exp statistics

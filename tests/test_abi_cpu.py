@@ -55,7 +55,7 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert lib.lpt_assign(cost, 3, 2, bins, load) == sxattn.SXA_EINVAL
     # attention: head_dim 96 unsupported, hq not a multiple of hkv, bad scale
     args = [null, null, null, 1, 1, 16, 4, 2, 96, 0.1, null, null, null, null, 0, 0, null, null,
-            null, 1, null, null]
+            null, 1, null, null, 0, null]
     assert lib.sparse_xattn_fwd(*args) == sxattn.SXA_EUNSUPPORTED
     args[8], args[6], args[7] = 128, 6, 4
     assert lib.sparse_xattn_fwd(*args) == sxattn.SXA_EINVAL

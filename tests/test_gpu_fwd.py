@@ -333,3 +333,35 @@ def test_context_gather_bit_exact(row_shape, dtype):
     torch.cuda.synchronize()
     want = src.cpu()[torch.as_tensor(synth.chunk_rows(gs, gl))]
     assert torch.equal(out.cpu(), want)
+
+
+def test_fwd_and_dq_dispatch_order_does_not_change_results():
+    """With a workspace the row groups are dispatched most-tiles-first; every row
+    group is still computed by one workgroup, so O, lse and the dQ accumulation are
+    bitwise identical to index-order dispatch."""
+    w = W["fwd_bf16_8kq_64k"]
+    gs, gl = np.array([0, 20480, 40960], np.int32), np.array([4096, 8192, 6144], np.int32)
+    meta, inp = fwd_case(w, 5, gs, gl)
+    blocks = np.arange(0, meta.n_blk, 5)[:96]  # 24 row groups of unequal cost
+    meta_sub = sub_blocks(meta, blocks)
+    rows = torch.from_numpy(token_rows(blocks)).cuda()
+    q = dev(inp.q)[rows].contiguous()
+    ks, vs = dev(inp.k_self)[rows].contiguous(), dev(inp.v_self)[rows].contiguous()
+    dm = device_meta(meta_sub, gs, gl)
+    scale = 1.0 / math.sqrt(w.d)
+    k, v = dev(inp.k), dev(inp.v)
+    o1, l1 = sxattn.sparse_xattn_fwd(q, k, v, dm, scale, ks, vs, workspace=None)
+    o2, l2 = sxattn.sparse_xattn_fwd(q, k, v, dm, scale, ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    do = torch.randn(o1.shape, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16).cuda()
+    delta = torch.empty((2,) + tuple(l1.shape), dtype=torch.float32, device="cuda")
+    dqs = []
+    for ws in (None, "auto"):
+        dq = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+        sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o1, do, l1, dq, ks, vs, delta_ws=delta,
+                                flags=sxattn.BWD_DELTA | sxattn.BWD_DQ, workspace=ws)
+        dqs.append(dq)
+    torch.cuda.synchronize()
+    assert torch.equal(dqs[0], dqs[1])
+    assert dqs[0].abs().max() > 0
