@@ -828,47 +828,53 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
   }
 }
 
-// Stream-K fix-up: one workgroup per (tile, kv head).  Tiles no step hits get
-// dK = dV = 0; tiles split over several shares get the sum of those shares' slots.
+// Stream-K fix-up: kRedParts workgroups per (tile, kv head), each over a contiguous
+// part of the tile's dK, dV rows.  Tiles no step hits get dK = dV = 0; tiles split
+// over several shares get the sum of those shares' slots.
+constexpr int kRedParts = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, DkdvSched sc) {
-  const int g = blockIdx.x % p.hkv;
-  const int t = blockIdx.x / p.hkv;
+  constexpr int V4 = kKeysPerWG * 2 * D / 4;  // float4 of one tile's dK, dV
+  constexpr int PER = V4 / kRedParts;
+  static_assert(PER % 256 == 0, "parts must split evenly over the threads");
+  const int part = blockIdx.x % kRedParts;
+  const int g = (blockIdx.x / kRedParts) % p.hkv;
+  const int t = blockIdx.x / kRedParts / p.hkv;
   const bool self_tile = t >= sc.n_ctx_tiles;
   const int64_t n_q = static_cast<int64_t>(p.n_blk) * kBlock;
   const int64_t key_rows = self_tile ? n_q : p.n_loc;
   const int64_t krow0 = static_cast<int64_t>(self_tile ? t - sc.n_ctx_tiles : t) * kKeysPerWG;
   float* dK = self_tile ? p.dk_self : p.dk;
   float* dV = self_tile ? p.dv_self : p.dv;
-  const int64_t W = sc.prefix[sc.n_tiles];
-  const int hits = sc.prefix[t + 1] - sc.prefix[t];
-  constexpr int V4 = kKeysPerWG * 2 * D / 4;
-  if (hits == 0) {
-    for (int i = threadIdx.x; i < V4; i += 256) {
-      const int e = 4 * i;
-      const int krow = e / (2 * D), which = (e / D) % 2, dcol = e % D;
-      const int64_t kr = krow0 + krow;
-      if (kr >= key_rows) continue;
-      *reinterpret_cast<f32x4*>((which == 0 ? dK : dV) + (kr * p.hkv + g) * D + dcol) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    return;
-  }
+  const int64_t W = ld_uniform(sc.prefix, sc.n_tiles);
+  const int t0 = ld_uniform(sc.prefix, t);
+  const int hits = ld_uniform(sc.prefix, t + 1) - t0;
+  int64_t j0 = 0, j1 = 0;
+  bool j0_later = false;
   const int64_t tot = W * p.hkv, ns = sc.n_shares;
-  const int64_t G0 = static_cast<int64_t>(g) * W + sc.prefix[t], G1 = G0 + hits;
-  // share j covers [floor(j tot / ns), floor((j + 1) tot / ns)); share holding x:
-  const int64_t j0 = ((G0 + 1) * ns - 1) / tot, j1 = (G1 * ns - 1) / tot;
-  if (j0 == j1) return;  // one share covered the whole tile and wrote it
-  const bool j0_later = j0 * tot / ns < G0;  // the tile is not share j0's first segment
+  if (hits > 0) {
+    const int64_t G0 = static_cast<int64_t>(g) * W + t0, G1 = G0 + hits;
+    // share j covers [floor(j tot / ns), floor((j + 1) tot / ns)); share holding x:
+    j0 = ((G0 + 1) * ns - 1) / tot;
+    j1 = (G1 * ns - 1) / tot;
+    if (j0 == j1) return;  // one share covered the whole tile and wrote it
+    j0_later = j0 * tot / ns < G0;  // the tile is not share j0's first segment
+  }
   const int64_t slot_elems = static_cast<int64_t>(kKeysPerWG) * 2 * D;
-  for (int i = threadIdx.x; i < V4; i += 256) {
+#pragma unroll 2
+  for (int i = part * PER + threadIdx.x; i < (part + 1) * PER; i += 256) {
     const int e = 4 * i;
     const int krow = e / (2 * D), which = (e / D) % 2, dcol = e % D;
     const int64_t kr = krow0 + krow;
     if (kr >= key_rows) continue;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(sc.slots + (2 * j0 + (j0_later ? 1 : 0)) * slot_elems + e);
-    for (int64_t j = j0 + 1; j <= j1; ++j)
-      if ((j + 1) * tot / ns > j * tot / ns)  // empty shares (list shorter than the grid) wrote nothing
-        acc += *reinterpret_cast<const f32x4*>(sc.slots + 2 * j * slot_elems + e);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (hits > 0) {
+      acc = *reinterpret_cast<const f32x4*>(sc.slots + (2 * j0 + (j0_later ? 1 : 0)) * slot_elems + e);
+      for (int64_t j = j0 + 1; j <= j1; ++j)
+        if ((j + 1) * tot / ns > j * tot / ns)  // empty shares (list shorter than the grid) wrote nothing
+          acc += *reinterpret_cast<const f32x4*>(sc.slots + 2 * j * slot_elems + e);
+    }
     *reinterpret_cast<f32x4*>((which == 0 ? dK : dV) + (kr * p.hkv + g) * D + dcol) = which == 0 ? acc * p.scale : acc;
   }
 }
@@ -976,7 +982,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     dkdv_bf16_kernel<D><<<dim3(static_cast<unsigned>(L.n_shares)), dim3(64 * kKvWaves), 0, s>>>(p, sc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dkdv_reduce_kernel<D><<<dim3(static_cast<unsigned>(n_tiles * a.hkv)), dim3(256), 0, s>>>(p, sc);
+    dkdv_reduce_kernel<D><<<dim3(static_cast<unsigned>(n_tiles * a.hkv * kRedParts)), dim3(256), 0, s>>>(p, sc);
     return hipGetLastError();
   }
   dkdv_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_tiles * a.hkv)), dim3(64 * kKvWaves), 0, s>>>(p, sc);
