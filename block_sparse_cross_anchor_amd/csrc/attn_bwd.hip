@@ -351,11 +351,17 @@ constexpr int kKeysPerWG = kKeysPerWave * kKvWaves;
 constexpr int kStepRows = 32;
 constexpr int kListCap = 2 * 64 * kKvWaves;  // step indices held in LDS at once
 
+// Stream-K list units: a tile with hits occupies kSetupUnits + hits consecutive units
+// of the per-head list (the first ones stand for its setup and write-back, so that a
+// share that starts many short tiles gets fewer steps); a tile without hits, none.
+constexpr int kSetupUnits = 3;
+
 struct DkdvSched {
   int32_t n_ctx_tiles, n_tiles;
   int32_t n_shares;        // stream-K workgroups; 0: one workgroup per (tile, kv head)
-  const int32_t* prefix;   // [n_tiles + 1]: first list position of each tile (per kv head)
-  const int32_t* krange;   // [n_tiles][2]: key-coordinate range of each tile
+  const int32_t* prefix;   // [n_tiles + 1]: first list unit of each tile (per kv head)
+  const int4* tinfo;       // [n_tiles]: key-coordinate range (x, y) and hit steps (z) of each tile
+  const int32_t* coord;    // [n_loc]: global key coordinate of each local context row
   float* slots;            // [2 n_shares][kKeysPerWG][2][D]: partial dK, dV
 };
 
@@ -412,7 +418,7 @@ __device__ __forceinline__ bool step_hit(const BwdParams& p, const StepGeo& sg, 
 
 // Count pass: one workgroup (256 threads, one per key row) per tile.
 __global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched sc, int32_t* prefix,
-                                                         int32_t* krange) {
+                                                         int4* tinfo, int32_t* coord) {
   __shared__ int red[2][4];
   const int t = blockIdx.x, tid = threadIdx.x, wave = tid / 64;
   const bool self_tile = t >= sc.n_ctx_tiles;
@@ -422,6 +428,7 @@ __global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched 
   const int64_t kr = static_cast<int64_t>(self_tile ? t - sc.n_ctx_tiles : t) * kKeysPerWG + tid;
   const bool valid = kr < key_rows;
   const int c = valid ? key_coord(p, self_tile, kr) : 0;
+  if (valid && !self_tile) coord[kr] = c;
   int kmin = valid ? c : 0x7fffffff, kmax = valid ? c : -0x7fffffff;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -439,9 +446,8 @@ __global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched 
   for (int base = 0; base < sg.n_steps; base += 256)
     n += __syncthreads_count(step_hit(p, sg, base + tid, n_q, self_tile, kmin, kmax));
   if (tid == 0) {
-    prefix[t + 1] = n;
-    krange[2 * t] = kmin;
-    krange[2 * t + 1] = kmax;
+    prefix[t + 1] = n > 0 ? n + kSetupUnits : 0;
+    tinfo[t] = int4{kmin, kmax, n, 0};
     if (t == 0) prefix[0] = 0;
   }
 }
@@ -485,6 +491,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
   __shared__ __attribute__((aligned(256))) uint16_t stg[3][SE];
   __shared__ __attribute__((aligned(16))) float smeta[3][2 * kStepRows];  // lse2 rows, delta rows
   __shared__ int step_list[kListCap];
+  __shared__ int4 step_iv[kListCap];  // key intervals of the listed step's two blocks
   __shared__ int wave_cnt[kWaves];
   __shared__ int red[2][kWaves];
 
@@ -505,17 +512,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
     pos = share * tot / sc.n_shares;
     end = (share + 1) * tot / sc.n_shares;
   }
-  const int64_t share_start = pos;
-
   // element row (token * hq + head) of step row `row` relative to the step's start
   auto row_elem = [&](int row, int g) {
     const int r = min(row, (sg.hcs == 1 ? sg.ts * sg.gs : kStepRows) - 1);
     return (r / sg.gs) * p.hq + g * grp + r % sg.gs;
   };
 
+  bool first_seg = true;  // no segment with steps yet in this share
   while (pos < end) {
     int g, t, s0, s1, hits = 0;
-    const int64_t seg_start = pos;
+    int kmin, kmax;
     if (streamk) {
       g = static_cast<int>(pos / W);
       const int r = static_cast<int>(pos % W);
@@ -526,11 +532,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
         else hi = mid;
       }
       t = lo;
-      const int t0 = ld_uniform(sc.prefix, t), t1 = ld_uniform(sc.prefix, t + 1);
-      hits = t1 - t0;
-      s0 = r - t0;
-      s1 = static_cast<int>(min<int64_t>(t1, r + (end - pos)) - t0);
-      pos += s1 - s0;
+      const int u0 = ld_uniform(sc.prefix, t) + kSetupUnits, u1 = ld_uniform(sc.prefix, t + 1);
+      const int ue = static_cast<int>(min<int64_t>(u1, r + (end - pos)));  // end of this share in the tile
+      pos += ue - r;
+      if (max(r, u0) >= ue) continue;  // only the tile's setup units fall in this share
+      const int4 ti = sc.tinfo[t];
+      kmin = __builtin_amdgcn_readfirstlane(ti.x);
+      kmax = __builtin_amdgcn_readfirstlane(ti.y);
+      hits = __builtin_amdgcn_readfirstlane(ti.z);
+      s0 = max(r, u0) - u0;
+      s1 = ue - u0;
     } else {
       g = blockIdx.x % p.hkv;
       t = blockIdx.x / p.hkv;
@@ -551,14 +562,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
       krow[hh] = kKeysPerWave * wave + 32 * hh + l32;
       kvalid[hh] = krow0 + krow[hh] < key_rows;
       krc[hh] = kvalid[hh] ? krow0 + krow[hh] : key_rows - 1;
-      kcoord[hh] = key_coord(p, self_tile, krc[hh]);
     }
-    int kmin, kmax;
     __syncthreads();  // the previous segment is done with vtile, red, the list and the stages
-    if (streamk) {
-      kmin = ld_uniform(sc.krange, 2 * t);
-      kmax = ld_uniform(sc.krange, 2 * t + 1);
-    } else {
+    {  // V rows of the tile -> LDS (direct copies into the swizzled layout)
+      const uint16_t* V = self_tile ? p.v_self : p.v;
+      constexpr int VI = kKeysPerWG * CPR / kT;  // copies per lane
+#pragma unroll
+      for (int j = 0; j < VI; ++j) {
+        const int inst = wave * VI + j;
+        const int c = inst * 64 + lane, row = c / CPR;
+        const int logical = (c % CPR) ^ LdsTile<D>::swz(row);
+        const int64_t src_row = min(krow0 + row, key_rows - 1);
+        dma16(V + (src_row * p.hkv + g) * D + 8 * logical, lds_addr(vtile + inst * 512));
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh)
+      kcoord[hh] = self_tile ? static_cast<int>(krc[hh]) : (streamk ? sc.coord[krc[hh]] : key_coord(p, false, krc[hh]));
+    if (!streamk) {
       kmin = 0x7fffffff;
       kmax = -0x7fffffff;
 #pragma unroll
@@ -585,15 +606,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
       }
     }
 
-    // V rows of the tile -> LDS; K of this wave's keys -> registers
-    {
-      const uint16_t* V = self_tile ? p.v_self : p.v;
-      for (int idx = tid; idx < kKeysPerWG * CPR; idx += kT) {
-        const int row = idx / CPR, j = idx % CPR;
-        const int64_t src_row = min(krow0 + row, key_rows - 1);
-        LdsTile<D>::store(vtile, row, j, *reinterpret_cast<const u32x4*>(V + (src_row * p.hkv + g) * D + 8 * j));
-      }
-    }
+    // K of this wave's keys -> registers
     bf16x8 kf[H][KS];
     {
       const uint16_t* K = self_tile ? p.k_self : p.k;
@@ -653,7 +666,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
         }
         const int o = ord + pre + __popcll(m & ((uint64_t{1} << lane) - 1));
         const int first = max(ord, s0);
-        if (hit && o >= s0 && o < s1) step_list[cnt + o - first] = st;
+        if (hit && o >= s0 && o < s1) {
+          const int tk = sg.tok0(st);
+          const int b0 = tk / kBlock, b1 = (tk + sg.ntok(st, n_q) - 1) / kBlock;
+          step_list[cnt + o - first] = st;
+          step_iv[cnt + o - first] =
+              self_tile ? int4{kBlock * b0, kBlock * b0 + kBlock, kBlock * b1, kBlock * b1 + kBlock}
+                        : int4{p.sample_start[b0], p.anchor[b0], p.sample_start[b1], p.anchor[b1]};
+        }
         cnt += max(0, min(ord + tot, s1) - first);
         ord += tot;
         scan += kT;
@@ -661,7 +681,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
       }
 
       // ---- three-stage pipeline over the listed steps: iteration i waits for step
-      // i, copies step i + 2 into the stage step i - 1 used, then computes step i
+      // i, copies step i + 2 into the stage step i - 1 used, then computes step i.
+      // Nothing else may be in flight: the waits below count only the copies.
+      wait_vmcnt<0>();
       for (int i = -2; i < cnt; ++i) {
         if (i >= 0) {
           if (i + 1 < cnt) {  // this wave's copies of step i landed; step i + 1 may fly
@@ -698,12 +720,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
         const int tk = sg.tok0(st);
         const int rmax = sg.rows(st, n_q, grp);
         const int b0 = tk / kBlock;
-        const int b1 = (tk + sg.ntok(st, n_q) - 1) / kBlock;
         const int split = (kBlock * (b0 + 1) - tk) * sg.gs;  // rows < split are in block b0
-        const int lo0 = self_tile ? kBlock * b0 : ld_uniform(p.sample_start, b0);
-        const int hi0 = self_tile ? kBlock * b0 + kBlock : ld_uniform(p.anchor, b0);
-        const int lo1 = self_tile ? kBlock * b1 : ld_uniform(p.sample_start, b1);
-        const int hi1 = self_tile ? kBlock * b1 + kBlock : ld_uniform(p.anchor, b1);
+        const int4 iv = step_iv[i];
+        const int lo0 = __builtin_amdgcn_readfirstlane(iv.x), hi0 = __builtin_amdgcn_readfirstlane(iv.y);
+        const int lo1 = __builtin_amdgcn_readfirstlane(iv.z), hi1 = __builtin_amdgcn_readfirstlane(iv.w);
         bool ok0[H], ok1[H], any = false, all = true;
 #pragma unroll
         for (int hh = 0; hh < H; ++hh) {
@@ -801,8 +821,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
     const bool whole = !streamk || (s0 == 0 && s1 == hits);
     float* slot = nullptr;
     if (!whole)
-      slot = sc.slots + (2 * static_cast<int64_t>(share) + (seg_start == share_start ? 0 : 1)) *
+      slot = sc.slots + (2 * static_cast<int64_t>(share) + (first_seg ? 0 : 1)) *
                             (static_cast<int64_t>(kKeysPerWG) * 2 * D);
+    first_seg = false;
 #pragma unroll
     for (int hh = 0; hh < H; ++hh) {
       if (!kvalid[hh]) continue;
@@ -849,17 +870,19 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, DkdvSched
   float* dV = self_tile ? p.dv_self : p.dv;
   const int64_t W = ld_uniform(sc.prefix, sc.n_tiles);
   const int t0 = ld_uniform(sc.prefix, t);
-  const int hits = ld_uniform(sc.prefix, t + 1) - t0;
+  const int hits = sc.tinfo[t].z;
   int64_t j0 = 0, j1 = 0;
   bool j0_later = false;
   const int64_t tot = W * p.hkv, ns = sc.n_shares;
   if (hits > 0) {
-    const int64_t G0 = static_cast<int64_t>(g) * W + t0, G1 = G0 + hits;
+    // the tile's steps are list units [G0, G1) of the flattened (head, tile) list
+    const int64_t G0 = static_cast<int64_t>(g) * W + t0 + kSetupUnits, G1 = G0 + hits;
     // share j covers [floor(j tot / ns), floor((j + 1) tot / ns)); share holding x:
     j0 = ((G0 + 1) * ns - 1) / tot;
     j1 = (G1 * ns - 1) / tot;
     if (j0 == j1) return;  // one share covered the whole tile and wrote it
-    j0_later = j0 * tot / ns < G0;  // the tile is not share j0's first segment
+    // share j0 had steps of an earlier tile when it starts before this tile's units
+    j0_later = j0 * tot / ns < G0 - kSetupUnits;
   }
   const int64_t slot_elems = static_cast<int64_t>(kKeysPerWG) * 2 * D;
 #pragma unroll 2
@@ -891,7 +914,7 @@ int n_compute_units() {
 }
 
 struct WsLayout {
-  int64_t n_tiles, n_shares, prefix_off, krange_off, order_off, slots_off, bytes;
+  int64_t n_tiles, n_shares, prefix_off, tinfo_off, coord_off, order_off, slots_off, bytes;
 };
 
 WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d, int64_t grp) {
@@ -901,8 +924,9 @@ WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d, int64_t grp) {
   L.n_shares = n_compute_units();
   const int64_t groups = (n_blk * kBlock * grp + kRowsPerGroup - 1) / kRowsPerGroup;
   L.prefix_off = 0;
-  L.krange_off = up(4 * (L.n_tiles + 1));
-  L.order_off = L.krange_off + up(8 * L.n_tiles);
+  L.tinfo_off = up(4 * (L.n_tiles + 1));
+  L.coord_off = L.tinfo_off + up(16 * L.n_tiles);
+  L.order_off = L.coord_off + up(4 * n_loc);
   L.slots_off = L.order_off + up(4 * (groups < kMaxOrderedGroups ? groups : int64_t{kMaxOrderedGroups}));
   L.bytes = L.slots_off + 2 * L.n_shares * static_cast<int64_t>(kKeysPerWG) * 2 * d * 4;
   return L;
@@ -965,18 +989,21 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   sc.n_tiles = static_cast<int32_t>(n_tiles);
   sc.n_shares = 0;
   sc.prefix = nullptr;
-  sc.krange = nullptr;
+  sc.tinfo = nullptr;
+  sc.coord = nullptr;
   sc.slots = nullptr;
   if (a.workspace != nullptr) {
     const WsLayout L = ws_layout(a.n_blk, a.n_loc, D, a.hq / a.hkv);
     char* ws = static_cast<char*>(a.workspace);
     int32_t* prefix = reinterpret_cast<int32_t*>(ws + L.prefix_off);
-    int32_t* krange = reinterpret_cast<int32_t*>(ws + L.krange_off);
+    int4* tinfo = reinterpret_cast<int4*>(ws + L.tinfo_off);
+    int32_t* coord = reinterpret_cast<int32_t*>(ws + L.coord_off);
     sc.n_shares = static_cast<int32_t>(L.n_shares);
     sc.prefix = prefix;
-    sc.krange = krange;
+    sc.tinfo = tinfo;
+    sc.coord = coord;
     sc.slots = reinterpret_cast<float*>(ws + L.slots_off);
-    dkdv_count_kernel<<<dim3(static_cast<unsigned>(n_tiles)), dim3(256), 0, s>>>(p, sc, prefix, krange);
+    dkdv_count_kernel<<<dim3(static_cast<unsigned>(n_tiles)), dim3(256), 0, s>>>(p, sc, prefix, tinfo, coord);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     dkdv_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(prefix, static_cast<int>(n_tiles));
     if ((e = hipGetLastError()) != hipSuccess) return e;
