@@ -354,7 +354,7 @@ constexpr int kListCap = 2 * 64 * kKvWaves;  // step indices held in LDS at once
 // Stream-K list units: a tile with hits occupies kSetupUnits + hits consecutive units
 // of the per-head list (the first ones stand for its setup and write-back, so that a
 // share that starts many short tiles gets fewer steps); a tile without hits, none.
-constexpr int kSetupUnits = 3;
+constexpr int kSetupUnits = 5;
 
 struct DkdvSched {
   int32_t n_ctx_tiles, n_tiles;
@@ -734,8 +734,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
         }
         if (!__any(any)) continue;
         const bool all_ok = rmax == kStepRows && __all(all);
-        const uint16_t* lq = stg[sb];
-        const uint16_t* ld = stg[sb] + kStepRows * D;
+        // Per-step LDS base addresses: stage bases are 16 KB aligned, so the k-step
+        // parts of the swizzled offsets (XOR constants) apply to base + offset; the
+        // dO rows (+ 32 D * 2 bytes) and later k-steps of the transposed reads are
+        // immediate offsets.
+        constexpr uint32_t kDoOff = kStepRows * D * 2;
+        const uint32_t stage = lds_addr(stg[sb]);
+        const uint32_t qb = stage + f_q, ta = stage + t_a, tb = stage + t_b;
+        const uint32_t vbase = lds_addr(vtile) + f_v;
         f32x16 sacc[H], pacc[H];
 #pragma unroll
         for (int hh = 0; hh < H; ++hh)
@@ -743,10 +749,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
           for (int i2 = 0; i2 < 16; ++i2) sacc[hh][i2] = pacc[hh][i2] = 0.f;
         // operands are read one k-step ahead; the scheduling barriers keep the compiler
         // from hoisting every k-step's reads (register pressure)
-        bf16x8 qa = LdsTile<D>::frag_at(lq, f_q), da = LdsTile<D>::frag_at(ld, f_q);
+        bf16x8 qa = lds_frag(qb), da = lds_frag(qb + kDoOff);
         bf16x8 vb[H];
 #pragma unroll
-        for (int hh = 0; hh < H; ++hh) vb[hh] = LdsTile<D>::frag_at(vtile + hh * 32 * D, f_v);
+        for (int hh = 0; hh < H; ++hh) vb[hh] = lds_frag(vbase + hh * 64 * D);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8 cq = qa, cd = da;
@@ -754,11 +760,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
 #pragma unroll
           for (int hh = 0; hh < H; ++hh) cv[hh] = vb[hh];
           if (ks + 1 < KS) {
-            const int o = f_q ^ (32 * (ks + 1)), ov = f_v ^ (32 * (ks + 1));
-            qa = LdsTile<D>::frag_at(lq, o);
-            da = LdsTile<D>::frag_at(ld, o);
+            const uint32_t o = qb ^ (32 * (ks + 1)), ov = vbase ^ (32 * (ks + 1));
+            qa = lds_frag(o);
+            da = lds_frag(o + kDoOff);
 #pragma unroll
-            for (int hh = 0; hh < H; ++hh) vb[hh] = LdsTile<D>::frag_at(vtile + hh * 32 * D, ov);
+            for (int hh = 0; hh < H; ++hh) vb[hh] = lds_frag(ov + hh * 64 * D);
           }
 #pragma unroll
           for (int hh = 0; hh < H; ++hh) {
@@ -767,25 +773,37 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+        // exponent S scale log2 e - lse2, in place
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&smeta[sb][8 * j + 4 * h2]);  // rows 8 j + 4 h2 + 0..3
+#pragma unroll
+          for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) sacc[hh][4 * j + i2] = fmaf(sacc[hh][4 * j + i2], p.scale_log2, -l4[i2]);
+        }
+        if (!all_ok) {  // keys outside a row's interval (and padding rows) get exp2(-inf) = 0
+#pragma unroll
+          for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int c = 8 * (r / 4) + r % 4;  // row 8 j + rel + i
+              const bool ok = (rel < split - c ? ok0[hh] : ok1[hh]) && rel < rmax - c;
+              sacc[hh][r] = ok ? sacc[hh][r] : -INFINITY;
+            }
+        }
+        // P = exp2(.) and dS = P (dP - delta) as bf16 pairs
         u32x4 pw[H][2], sw[H][2];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // rows 8 j + 4 h2 + 0..3 of the step
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&smeta[sb][8 * j + 4 * h2]);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(&smeta[sb][kStepRows + 8 * j + 4 * h2]);
 #pragma unroll
           for (int hh = 0; hh < H; ++hh) {
             float pr[4], ds[4];
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2) {
-              const int r = 4 * j + i2;
-              pr[i2] = __builtin_amdgcn_exp2f(fmaf(sacc[hh][r], p.scale_log2, -l4[i2]));
-              if (!all_ok) {  // row 8 j + rel + i2: compare rel with step-uniform bounds
-                const int c = 8 * j + i2;
-                const bool ok = (rel < split - c ? ok0[hh] : ok1[hh]) && rel < rmax - c;
-                pr[i2] = ok ? pr[i2] : 0.f;
-              }
-              ds[i2] = pr[i2] * (pacc[hh][r] - d4[i2]);
+              pr[i2] = __builtin_amdgcn_exp2f(sacc[hh][4 * j + i2]);
+              ds[i2] = pr[i2] * (pacc[hh][4 * j + i2] - d4[i2]);
             }
             pw[hh][j / 2][2 * (j % 2)] = pack_bf16x2(pr[0], pr[1]);
             pw[hh][j / 2][2 * (j % 2) + 1] = pack_bf16x2(pr[2], pr[3]);
@@ -793,16 +811,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
             sw[hh][j / 2][2 * (j % 2) + 1] = pack_bf16x2(ds[2], ds[3]);
           }
         }
-        bf16x8 dta = LdsTile<D>::frag_t_at(ld, t_a, t_b), qta = LdsTile<D>::frag_t_at(lq, t_a, t_b);
+        bf16x8 dta = lds_frag_t(ta + kDoOff, tb + kDoOff), qta = lds_frag_t(ta, tb);
 #pragma unroll
         for (int kd = 0; kd < 2 * DT; ++kd) {
           const int kq = kd / DT, dt = kd % DT;
           const bf16x8 cdt = dta, cqt = qta;
           if (kd + 1 < 2 * DT) {
             const int kq1 = (kd + 1) / DT, dt1 = (kd + 1) % DT;
-            const int oa = (t_a ^ (64 * dt1)) + kq1 * 32 * D, ob = (t_b ^ (64 * dt1)) + kq1 * 32 * D;
-            dta = LdsTile<D>::frag_t_at(ld, oa, ob);
-            qta = LdsTile<D>::frag_t_at(lq, oa, ob);
+            const uint32_t oa = (ta ^ (64 * dt1)) + kq1 * 32 * D, ob = (tb ^ (64 * dt1)) + kq1 * 32 * D;
+            dta = lds_frag_t(oa + kDoOff, ob + kDoOff);
+            qta = lds_frag_t(oa, ob);
           }
 #pragma unroll
           for (int hh = 0; hh < H; ++hh) {

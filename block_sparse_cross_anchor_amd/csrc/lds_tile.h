@@ -82,6 +82,19 @@ struct LdsTile {
   }
 };
 
+// Reads at raw LDS byte addresses (32-bit, as lds_addr() gives them), for loops that
+// keep one per-lane base address and vary it by XOR / immediate offsets.
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+__device__ __forceinline__ bf16x8 lds_frag(uint32_t addr) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<lds_u32x4*>(addr));
+}
+__device__ __forceinline__ bf16x8 lds_frag_t(uint32_t addr_a, uint32_t addr_b) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(addr_a));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(addr_b));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return __builtin_bit_cast(bf16x8, u32x4{ua[0], ua[1], ub[0], ub[1]});
+}
+
 // Key order shared by P (or dS) held in MFMA accumulator registers and the
 // transposed operand that multiplies it: in k-step ks (16 keys) lane half h holds,
 // at positions i = 0..7, the keys 16 ks + 8 (i / 4) + 4 h + i % 4.  frag_t reads
