@@ -22,12 +22,12 @@
 // cross-workgroup reductions of dQ.
 #include "device_common.h"
 #include "internal.h"
+#include "kv_walk.h"
 #include "lds_tile.h"
 
 namespace sxa {
 namespace {
 
-constexpr int kTileKeys = 64;
 #ifndef SXA_DQ_WAVES
 #define SXA_DQ_WAVES 8
 #endif
@@ -77,112 +77,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // ============================================================================ dq kernel
-
-struct Tile {
-  int64_t row0;
-  int nrows;
-  int coord0;
-  int self;
-};
-
-struct Walk {
-  int self_pos, self_end;
-  int c;
-  int64_t off;
-  int gs, len, t, t_end;
-};
-
-__device__ __forceinline__ bool walk_next(Walk& w, const int32_t* __restrict__ cgs,
-                                          const int32_t* __restrict__ clen, int n_chunk, int LO,
-                                          int HI, Tile& out) {
-  if (w.self_pos < w.self_end) {
-    out.row0 = w.self_pos;
-    out.nrows = min(kTileKeys, w.self_end - w.self_pos);
-    out.coord0 = w.self_pos;
-    out.self = 1;
-    w.self_pos += kTileKeys;
-    return true;
-  }
-  while (true) {
-    if (w.t < w.t_end) {
-      out.row0 = w.off + static_cast<int64_t>(w.t) * kTileKeys;
-      out.nrows = min(kTileKeys, w.len - w.t * kTileKeys);
-      out.coord0 = w.gs + w.t * kTileKeys;
-      out.self = 0;
-      ++w.t;
-      return true;
-    }
-    if (w.c >= n_chunk) return false;
-    w.off += w.len;
-    ++w.c;
-    if (w.c >= n_chunk) {
-      w.len = 0;
-      return false;
-    }
-    w.gs = cgs[w.c];
-    w.len = clen[w.c];
-    const int a = max(LO, w.gs), e = min(HI, w.gs + w.len);
-    if (a < e) {
-      w.t = (a - w.gs) / kTileKeys;
-      w.t_end = (e - w.gs + kTileKeys - 1) / kTileKeys;
-    } else {
-      w.t = w.t_end = 0;
-    }
-  }
-}
-
-// K and V tiles staged row-major (lds_tile.h); K^T for dQ comes from the
-// transposing read of the same K tile.
-template <int D, int kT>
-struct DqTileRegs {
-  static constexpr int CPR = D / 8;
-  static constexpr int CH = kTileKeys * CPR;
-  static constexpr int L = (CH + kT - 1) / kT;
-  u32x4 k[L], v[L];
-
-  __device__ __forceinline__ void load(const Tile& t, const BwdParams& p, int g, int tid) {
-    const uint16_t* K = t.self ? p.k_self : p.k;
-    const uint16_t* V = t.self ? p.v_self : p.v;
-    const int last = t.nrows - 1;
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int idx = tid + kT * i;
-      if (CH % kT == 0 || idx < CH) {
-        const int key = min(idx / CPR, last), j = idx % CPR;
-        const int64_t off = ((t.row0 + key) * p.hkv + g) * D + 8 * j;
-        k[i] = *reinterpret_cast<const u32x4*>(K + off);
-        v[i] = *reinterpret_cast<const u32x4*>(V + off);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* lk, uint16_t* lv, int tid) const {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int idx = tid + kT * i;
-      if (CH % kT == 0 || idx < CH) {
-        LdsTile<D>::store(lk, idx / CPR, idx % CPR, k[i]);
-        LdsTile<D>::store(lv, idx / CPR, idx % CPR, v[i]);
-      }
-    }
-  }
-};
+//
+// Query-major, same tiles as the forward: a workgroup of kDqWaves waves owns 256
+// query rows of one kv head (32 per wave, Q and dO held in registers as MFMA B
+// operands) and walks the 64-key tiles their blocks may read (kv_walk.h), copied
+// into LDS three tiles deep.  Per tile: S^T = K Q^T, dP^T = V dO^T, dS^T in
+// registers, dQ^T += K^T dS^T (K^T from the transposing read of the K tile).
 
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWaves))) void dq_bf16_kernel(
     BwdParams p) {
-  constexpr int kT = 64 * kDqWaves;
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int ROWS = 32 * kDqWaves;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileKeys * D];
+  using Dma = TileDma<D, kDqWaves>;
+  __shared__ __attribute__((aligned(256))) uint16_t bufs[3][Dma::ELEMS];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
   const int g = blockIdx.x % p.hkv;
   const int wg = p.rg_order ? p.rg_order[blockIdx.x / p.hkv] : static_cast<int>(blockIdx.x / p.hkv);
   const int grp = p.hq / p.hkv;
-  const int64_t R = static_cast<int64_t>(p.n_blk) * kBlock * grp;
+  const int64_t n_q = static_cast<int64_t>(p.n_blk) * kBlock;
+  const int64_t R = n_q * grp;
   const int64_t wg_row0 = static_cast<int64_t>(wg) * ROWS;
   const int64_t wg_last = min(wg_row0 + ROWS - 1, R - 1);
   const int b_first = static_cast<int>(wg_row0 / grp / kBlock);
@@ -192,15 +109,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
     LO = min(LO, p.sample_start[b]);
     HI = max(HI, p.anchor[b]);
   }
-
   Walk w;
-  w.self_pos = p.k_self ? kBlock * b_first : 0;
-  w.self_end = p.k_self ? kBlock * (b_last + 1) : 0;
-  w.c = -1;
-  w.off = 0;
-  w.gs = w.len = w.t = w.t_end = 0;
-  Tile cur, nxt;
-  bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
+  w.start(p.k_self != nullptr, b_first, b_last);
+  Tile cur;
+  const bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
 
   // this lane's query row (column of the 32-row N tile)
   const int64_t r = wg_row0 + 32 * wave + l32;
@@ -221,9 +133,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
   }
   const int clo = valid ? p.sample_start[blk] : 0, chi = valid ? p.anchor[blk] : 0;
   const int slo = valid ? kBlock * blk : 0, shi = valid ? kBlock * blk + kBlock : 0;
-  const float lse_nat = p.lse[orow];
-  // rows with no key at all contribute nothing: exp2(x - inf) = 0
-  const float lse2 = (valid && lse_nat != -INFINITY) ? lse_nat * kLog2e : INFINITY;
+  // lse in log2 units (+inf for rows without keys: exp2(x - inf) = 0), and delta
+  const float lse2 = valid ? p.delta[n_q * p.hq + orow] : INFINITY;
   const float dlt = p.delta[orow];
   bf16x8 qf[KS], df[KS];
 #pragma unroll
@@ -238,23 +149,40 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[dt][i] = 0.f;
 
-  DqTileRegs<D, kT> regs;
-  regs.load(cur, p, g, tid);
-  regs.store(lds[0][0], lds[0][1], tid);
-  __syncthreads();
-  int buf = 0;
-  while (have) {
-    const bool has_next = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, nxt);
-    if (has_next) regs.load(nxt, p, g, tid);
+  // LDS byte offsets within a tile buffer (see LdsTile): K / V rows 32 mt + l32,
+  // transposed K reads of the key steps
+  int f_k = LdsTile<D>::frag_off(l32, h2);
+  int t_a = LdsTile<D>::tr_off(4 * h2 + ((lane & 15) >> 2), (lane >> 4) & 1, lane & 15);
+  int t_b = LdsTile<D>::tr_off(8 + 4 * h2 + ((lane & 15) >> 2), (lane >> 4) & 1, lane & 15);
+  constexpr uint32_t kVOff = kTileKeys * D * 2;  // V rows follow the K rows
 
+  // Three-stage pipeline: tile t is computed from buffer t % 3 while the copies of
+  // tiles t + 1 and t + 2 are in flight.  The prologue's own loads complete first,
+  // so that the only vector-memory operations in flight in the loop are the copies.
+  wait_vmcnt<0>();
+  Tile n1, n2;
+  Dma::issue(cur, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[0]);
+  bool have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
+  if (have1) Dma::issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[1]);
+  int cb = 0;
+  while (true) {
+    if (have1) wait_vmcnt<Dma::NI>();  // this wave's copies of `cur` landed (n1 may fly)
+    else wait_vmcnt<0>();
+    barrier_nofence();                 // ... and every wave's; all reads of the third buffer are done
+    const bool have2 = have1 && walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);
+    if (have2) Dma::issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[cb == 0 ? 2 : cb - 1]);
+
+    // per-lane constants are redefined opaquely per tile so that derived addresses
+    // are recomputed rather than held
+    asm volatile("" : "+v"(f_k), "+v"(t_a), "+v"(t_b));
     const int lo = cur.self ? slo : clo, hi = cur.self ? shi : chi;
     const int a_lo = max(lo - cur.coord0, 0), a_hi = min(hi - cur.coord0, cur.nrows);
     const bool any = a_lo < a_hi;
     const bool full = (a_lo == 0) & (a_hi == kTileKeys);
     if (__any(any)) {
       const bool all_full = __all(full);
-      const uint16_t* lk = lds[buf][0];
-      const uint16_t* lv = lds[buf][1];
+      const uint32_t base = lds_addr(bufs[cb]);
+      const uint32_t kb = base + f_k, ta = base + t_a, tb = base + t_b;
       f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -262,44 +190,56 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
         for (int i = 0; i < 16; ++i) sacc[mt][i] = pacc[mt][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t o = kb ^ (32 * ks);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 kf = LdsTile<D>::frag(lk, 32 * mt + l32, 2 * ks + h2);
-          const bf16x8 vf = LdsTile<D>::frag(lv, 32 * mt + l32, 2 * ks + h2);
+          const bf16x8 kf = lds_frag(o + mt * 64 * D);
+          const bf16x8 vf = lds_frag(o + mt * 64 * D + kVOff);
           sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
           pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[ks], pacc[mt], 0, 0, 0);
         }
       }
-      bf16x8 dsf[4];
+      // exponent in place; keys outside the row's interval get exp2(-inf) = 0
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], p.scale_log2, -lse2));
-          if (!all_full) {
+        for (int i = 0; i < 16; ++i) sacc[mt][i] = fmaf(sacc[mt][i], p.scale_log2, -lse2);
+      if (!all_full) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
             const int key = 32 * mt + 8 * (i / 4) + 4 * h2 + (i % 4);
-            if (key < a_lo || key >= a_hi) pr = 0.f;
+            if (key < a_lo || key >= a_hi) sacc[mt][i] = -INFINITY;
           }
-          const float ds = pr * (pacc[mt][i] - dlt);
-          dsf[2 * mt + i / 8][i % 8] = static_cast<__bf16>(ds);
+      }
+      u32x4 dsw[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int i = 2 * q;
+          const float d0 = __builtin_amdgcn_exp2f(sacc[mt][i]) * (pacc[mt][i] - dlt);
+          const float d1 = __builtin_amdgcn_exp2f(sacc[mt][i + 1]) * (pacc[mt][i + 1] - dlt);
+          dsw[2 * mt + q / 4][q % 4] = pack_bf16x2(d0, d1);
         }
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int sl = lane & 15;
-          const bf16x8 kt = LdsTile<D>::frag_t(lk, tr_row_a(kq, h2, sl), tr_row_b(kq, h2, sl),
-                                               32 * dt + 16 * ((lane >> 4) & 1), sl);
-          dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, dsf[kq], dqacc[dt], 0, 0, 0);
+          const uint32_t oa = (ta ^ (64 * dt)) + kq * 32 * D, ob = (tb ^ (64 * dt)) + kq * 32 * D;
+          const bf16x8 kt = lds_frag_t(oa, ob);
+          dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, __builtin_bit_cast(bf16x8, dsw[kq]), dqacc[dt], 0,
+                                                              0, 0);
         }
       }
     }
 
-    if (has_next) regs.store(lds[buf ^ 1][0], lds[buf ^ 1][1], tid);
-    __syncthreads();
-    if (!has_next) break;
-    cur = nxt;
-    buf ^= 1;
+    if (!have1) break;
+    cur = n1;
+    n1 = n2;
+    have1 = have2;
+    cb = cb == 2 ? 0 : cb + 1;
   }
 
   if (!valid) return;

@@ -37,14 +37,13 @@
 // Online softmax in base 2: x = s * scale * log2(e); p = exp2(x - m).
 #include "device_common.h"
 #include "internal.h"
+#include "kv_walk.h"
 #include "lds_tile.h"
 
-#include <type_traits>
 
 namespace sxa {
 namespace {
 
-constexpr int kTileKeys = 64;
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
 struct FwdParams {
@@ -64,97 +63,7 @@ struct FwdParams {
   float scale_log2;  // scale * log2(e)
 };
 
-struct Tile {
-  int64_t row0;  // first source row (local K/V row, or own-block row)
-  int nrows;     // valid rows (<= 64)
-  int coord0;    // key coordinate of row0: global position, or own-block row index
-  int self;      // 1: own-block tile
-};
-
-// Sequence of key tiles of one workgroup (uniform across the workgroup).
-struct Walk {
-  int self_pos, self_end;
-  int c;
-  int64_t off;
-  int gs, len, t, t_end;
-};
-
-__device__ __forceinline__ bool walk_next(Walk& w, const int32_t* __restrict__ cgs,
-                                          const int32_t* __restrict__ clen, int n_chunk, int LO,
-                                          int HI, Tile& out) {
-  if (w.self_pos < w.self_end) {
-    out.row0 = w.self_pos;
-    out.nrows = min(kTileKeys, w.self_end - w.self_pos);
-    out.coord0 = w.self_pos;
-    out.self = 1;
-    w.self_pos += kTileKeys;
-    return true;
-  }
-  while (true) {
-    if (w.t < w.t_end) {
-      out.row0 = w.off + static_cast<int64_t>(w.t) * kTileKeys;
-      out.nrows = min(kTileKeys, w.len - w.t * kTileKeys);
-      out.coord0 = w.gs + w.t * kTileKeys;
-      out.self = 0;
-      ++w.t;
-      return true;
-    }
-    if (w.c >= n_chunk) return false;
-    w.off += w.len;
-    ++w.c;
-    if (w.c >= n_chunk) {
-      w.len = 0;
-      return false;
-    }
-    // uniform index + constant address space: scalar loads, counted apart from
-    // the vector-memory queue that the tile DMA uses
-    const int c = __builtin_amdgcn_readfirstlane(w.c);
-    w.gs = ((const __attribute__((address_space(4))) int32_t*)(cgs))[c];
-    w.len = ((const __attribute__((address_space(4))) int32_t*)(clen))[c];
-    const int a = max(LO, w.gs), e = min(HI, w.gs + w.len);
-    if (a < e) {
-      w.t = (a - w.gs) / kTileKeys;
-      w.t_end = (e - w.gs + kTileKeys - 1) / kTileKeys;
-    } else {
-      w.t = w.t_end = 0;
-    }
-  }
-}
-
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
-
-// One 64-key tile (K rows then V rows of one kv head) is copied straight from HBM
-// into a row-major LDS tile with global_load_lds_dwordx4: lane i of a wave writes
-// the 16 bytes at LDS offset 16 i of its 1 KiB slice, so each lane picks the
-// global chunk that belongs at that position under the tile's swizzle.  Rows past
-// the tile end are clamped to its last row (those keys are masked, any finite
-// value will do).  Every wave issues NI instructions per tile.
-template <int D, int WAVES>
-struct TileDma {
-  static constexpr int CPR = D / 8;
-  static constexpr int HALF = kTileKeys * CPR;   // chunks of K (or V) per tile
-  static constexpr int NI = 2 * HALF / 64 / WAVES;
-  static_assert(NI * 64 * WAVES == 2 * HALF, "tile must split evenly over the waves");
-  static constexpr int ELEMS = 2 * kTileKeys * D;  // bf16 per buffer
-
-  __device__ static __forceinline__ void issue(const Tile& t, const FwdParams& p, int g, int wave,
-                                               int lane, uint16_t* buf) {
-    const uint16_t* K = t.self ? p.k_self : p.k;
-    const uint16_t* V = t.self ? p.v_self : p.v;
-    const int last = t.nrows - 1;
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int inst = wave * NI + j;
-      const int c = inst * 64 + lane;
-      const bool isv = c >= HALF;  // uniform per instruction
-      const int cc = isv ? c - HALF : c;
-      const int row = cc / CPR;
-      const int logical = (cc % CPR) ^ LdsTile<D>::swz(row);
-      const uint16_t* src = (isv ? V : K) + ((t.row0 + min(row, last)) * p.hkv + g) * D + 8 * logical;
-      dma16(src, lds_addr(buf + inst * 512));
-    }
-  }
-};
 
 // NT: 32-row N tiles per wave (rows per wave = 32 * NT); WAVES: waves per workgroup.
 template <int D, int NT, int WAVES, bool OUT_BF16>
@@ -184,11 +93,7 @@ fwd_bf16_kernel(FwdParams p) {
   }
 
   Walk w;
-  w.self_pos = p.k_self ? kBlock * b_first : 0;
-  w.self_end = p.k_self ? kBlock * (b_last + 1) : 0;
-  w.c = -1;
-  w.off = 0;
-  w.gs = w.len = w.t = w.t_end = 0;
+  w.start(p.k_self != nullptr, b_first, b_last);
 
   float m[NT], l[NT];
   f32x16 oacc[DT][NT];
@@ -255,9 +160,9 @@ fwd_bf16_kernel(FwdParams p) {
   // so that the only vector-memory operations in flight in the loop are the DMA.
   wait_vmcnt<0>();
   Tile n1, n2;
-  Dma::issue(cur, p, g, wave, lane, bufs[0]);
+  Dma::issue(cur, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[0]);
   bool have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
-  if (have1) Dma::issue(n1, p, g, wave, lane, bufs[1]);
+  if (have1) Dma::issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[1]);
   int cb = 0;
   while (true) {
     const uint16_t* cbuf = bufs[cb];
@@ -266,7 +171,7 @@ fwd_bf16_kernel(FwdParams p) {
     else wait_vmcnt<0>();
     barrier_nofence();                 // ... and every wave's; all reads of pbuf are done
     const bool have2 = have1 && walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);
-    if (have2) Dma::issue(n2, p, g, wave, lane, pbuf);
+    if (have2) Dma::issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, pbuf);
       // ---- this wave's share of the tile
       int a_lo[NT], a_hi[NT];
       bool any = false, full = true;
