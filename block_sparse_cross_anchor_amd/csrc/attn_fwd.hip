@@ -46,6 +46,7 @@ namespace {
 
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
+
 struct FwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -66,15 +67,16 @@ struct FwdParams {
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
 // NT: 32-row N tiles per wave (rows per wave = 32 * NT); WAVES: waves per workgroup.
-template <int D, int NT, int WAVES, bool OUT_BF16>
+template <int D, int NT, int WAVES, int NSTAGE, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES))) void
 fwd_bf16_kernel(FwdParams p) {
+  static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three tile buffers");
   constexpr int T = 64 * WAVES;
   constexpr int ROWS = 32 * NT * WAVES;  // rows per workgroup
   constexpr int KS = D / 16;             // k-steps of S^T
   constexpr int DT = D / 32;             // 32-row d tiles of O^T
   using Dma = TileDma<D, WAVES>;
-  __shared__ __attribute__((aligned(16))) uint16_t bufs[3][Dma::ELEMS];
+  __shared__ __attribute__((aligned(256))) uint16_t bufs[NSTAGE][Dma::ELEMS];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
@@ -159,19 +161,37 @@ fwd_bf16_kernel(FwdParams p) {
   // tiles t + 1 and t + 2 is in flight.  The prologue's own loads complete first,
   // so that the only vector-memory operations in flight in the loop are the DMA.
   wait_vmcnt<0>();
+  // LDS byte offsets within a tile buffer (see LdsTile): K rows 32 mt + l32, and the
+  // transposed V reads of the key steps
+  int f_k = LdsTile<D>::frag_off(l32, h2);
+  int t_a = LdsTile<D>::tr_off(4 * h2 + ((lane & 15) >> 2), (lane >> 4) & 1, lane & 15);
+  int t_b = LdsTile<D>::tr_off(8 + 4 * h2 + ((lane & 15) >> 2), (lane >> 4) & 1, lane & 15);
+  constexpr uint32_t kVOff = kTileKeys * D * 2;  // V rows follow the K rows
   Tile n1, n2;
   Dma::issue(cur, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[0]);
-  bool have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
-  if (have1) Dma::issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[1]);
+  bool have1 = false;
+  if constexpr (NSTAGE == 3) {
+    have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
+    if (have1) Dma::issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[1]);
+  }
   int cb = 0;
   while (true) {
-    const uint16_t* cbuf = bufs[cb];
-    uint16_t* pbuf = bufs[cb == 0 ? 2 : cb - 1];
-    if (have1) wait_vmcnt<Dma::NI>();  // this wave's DMA of `cur` done (n1 may be in flight)
-    else wait_vmcnt<0>();
-    barrier_nofence();                 // ... and every wave's; all reads of pbuf are done
-    const bool have2 = have1 && walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);
-    if (have2) Dma::issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, pbuf);
+    bool have2 = false;
+    if constexpr (NSTAGE == 3) {
+      if (have1) wait_vmcnt<Dma::NI>();  // this wave's DMA of `cur` done (n1 may be in flight)
+      else wait_vmcnt<0>();
+      barrier_nofence();                 // ... and every wave's; all reads of the third buffer are done
+      have2 = have1 && walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);
+      if (have2) Dma::issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[cb == 0 ? 2 : cb - 1]);
+    } else {
+      wait_vmcnt<0>();
+      barrier_nofence();  // `cur` landed everywhere; the other buffer is no longer read
+      have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
+      if (have1) Dma::issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[cb ^ 1]);
+    }
+      // per-lane constants are redefined opaquely per tile so that derived addresses
+      // are recomputed rather than held
+      asm volatile("" : "+v"(f_k), "+v"(t_a), "+v"(t_b));
       // ---- this wave's share of the tile
       int a_lo[NT], a_hi[NT];
       bool any = false, full = true;
@@ -186,8 +206,8 @@ fwd_bf16_kernel(FwdParams p) {
       }
       if (__any(any)) {
         const bool all_full = __all(full);
-        const uint16_t* lk = cbuf;
-        const uint16_t* lv = cbuf + kTileKeys * D;
+        const uint32_t base = lds_addr(bufs[cb]);
+        const uint32_t kb = base + f_k, ta = base + t_a + kVOff, tb = base + t_b + kVOff;
         f32x16 sacc[2][NT];
   #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -199,7 +219,7 @@ fwd_bf16_kernel(FwdParams p) {
         for (int ks = 0; ks < KS; ++ks) {
   #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 kf = LdsTile<D>::frag(lk, 32 * mt + l32, 2 * ks + h2);
+            const bf16x8 kf = lds_frag((kb ^ (32 * ks)) + mt * 64 * D);
   #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
               sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], sacc[mt][nt], 0, 0, 0);
@@ -270,9 +290,7 @@ fwd_bf16_kernel(FwdParams p) {
         for (int kq = 0; kq < 4; ++kq) {
   #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const int sl = lane & 15;
-            const bf16x8 vf = LdsTile<D>::frag_t(lv, tr_row_a(kq, h2, sl), tr_row_b(kq, h2, sl),
-                                                 32 * dt + 16 * ((lane >> 4) & 1), sl);
+            const bf16x8 vf = lds_frag_t((ta ^ (64 * dt)) + kq * 32 * D, (tb ^ (64 * dt)) + kq * 32 * D);
   #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
               oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nt][kq], oacc[dt][nt], 0, 0, 0);
@@ -283,9 +301,13 @@ fwd_bf16_kernel(FwdParams p) {
 
     if (!have1) break;
     cur = n1;
-    n1 = n2;
-    have1 = have2;
-    cb = cb == 2 ? 0 : cb + 1;
+    if constexpr (NSTAGE == 3) {
+      n1 = n2;
+      have1 = have2;
+      cb = cb == 2 ? 0 : cb + 1;
+    } else {
+      cb ^= 1;
+    }
   }
 
   // ---- epilogue: normalise, write O and lse
@@ -318,10 +340,13 @@ fwd_bf16_kernel(FwdParams p) {
 #ifndef SXA_FWD_WAVES
 #define SXA_FWD_WAVES 8
 #endif
+#ifndef SXA_FWD_STAGES
+#define SXA_FWD_STAGES 3
+#endif
 constexpr int kNT = 1;                  // 32 query rows per wave
 constexpr int kWaves = SXA_FWD_WAVES;   // waves sharing each K/V tile
+constexpr int kStages = SXA_FWD_STAGES; // K/V tile buffers
 constexpr int kRowsPerWG = 32 * kNT * kWaves;
-static_assert(kRowsPerWG == kRowsPerGroup, "row groups are shared with the dispatch order");
 
 template <int D, bool OUT_BF16>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
@@ -348,14 +373,14 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   const int64_t n_wg = groups * a.hkv;
   if (n_wg == 0) return hipSuccess;
   if (p.rg_order != nullptr) {
-    if (groups > kMaxOrderedGroups) {
+    if (groups > kMaxOrderedGroups || kRowsPerWG != kRowsPerGroup) {
       p.rg_order = nullptr;
     } else {
       const hipError_t e = launch_row_group_order(a, kRowsPerWG, a.rg_order, s);
       if (e != hipSuccess) return e;
     }
   }
-  fwd_bf16_kernel<D, kNT, kWaves, OUT_BF16>
+  fwd_bf16_kernel<D, kNT, kWaves, kStages, OUT_BF16>
       <<<dim3(static_cast<unsigned>(n_wg)), dim3(64 * kWaves), 0, s>>>(p);
   return hipGetLastError();
 }
