@@ -287,6 +287,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
 // computed the copies of steps i+1 and i+2 are in flight; one barrier per step.
 
 constexpr int kKeysPerWave = 32 * kKvHalves;
+#ifndef SXA_KV_STEPS_PER_SYNC
+#define SXA_KV_STEPS_PER_SYNC 2
+#endif
+constexpr int kStepsPerSync = SXA_KV_STEPS_PER_SYNC;  // query steps between workgroup barriers
+constexpr int kStageBufs = 2 * kStepsPerSync;          // LDS stages: one group computed, one in flight
 constexpr int kKeysPerWG = kKeysPerWave * kKvWaves;
 constexpr int kStepRows = 32;
 constexpr int kListCap = 2 * 64 * kKvWaves;  // step indices held in LDS at once
@@ -428,8 +433,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
   static_assert(NI >= 1 && NI * kT == 2 * kStepRows * CPR, "stage copy must split evenly over lanes");
   constexpr int SE = 2 * kStepRows * D;  // elements of one stage: Q rows, then dO rows
   __shared__ __attribute__((aligned(256))) uint16_t vtile[kKeysPerWG * D];
-  __shared__ __attribute__((aligned(256))) uint16_t stg[3][SE];
-  __shared__ __attribute__((aligned(16))) float smeta[3][2 * kStepRows];  // lse2 rows, delta rows
+  __shared__ __attribute__((aligned(256))) uint16_t stg[kStageBufs][SE];
+  __shared__ __attribute__((aligned(16))) float smeta[kStageBufs][2 * kStepRows];  // lse2 rows, delta rows
   __shared__ int step_list[kListCap];
   __shared__ int4 step_iv[kListCap];  // key intervals of the listed step's two blocks
   __shared__ int wave_cnt[kWaves];
@@ -620,23 +625,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
         __syncthreads();
       }
 
-      // ---- three-stage pipeline over the listed steps: iteration i waits for step
-      // i, copies step i + 2 into the stage step i - 1 used, then computes step i.
-      // Nothing else may be in flight: the waits below count only the copies.
+      // ---- pipeline over the listed steps in groups of kStepsPerSync: iteration j
+      // waits for group j, copies group j + 1 into the stages group j - 1 used, then
+      // computes group j.  Nothing else may be in flight while the copies are counted.
       wait_vmcnt<0>();
-      for (int i = -2; i < cnt; ++i) {
-        if (i >= 0) {
-          if (i + 1 < cnt) {  // this wave's copies of step i landed; step i + 1 may fly
-            if (wave == 0) wait_vmcnt<NI + 1>();
-            else wait_vmcnt<NI>();
-          } else {
-            wait_vmcnt<0>();
-          }
-          barrier_nofence();  // every wave's copies landed; stage (i + 2) % 3 is free
+      const int ngrp = (cnt + kStepsPerSync - 1) / kStepsPerSync;
+      for (int jg = -1; jg < ngrp; ++jg) {
+        if (jg >= 0) {
+          wait_vmcnt<0>();    // this wave's copies of group jg landed
+          barrier_nofence();  // every wave's; group jg - 1's stages are no longer read
         }
-        if (i + 2 < cnt) {
-          const int nst = __builtin_amdgcn_readfirstlane(step_list[i + 2]);
-          const int sb2 = (i + 2) % 3;
+#pragma unroll
+        for (int q = 0; q < kStepsPerSync; ++q) {
+          const int si = (jg + 1) * kStepsPerSync + q;
+          if (jg + 1 >= ngrp || si >= cnt) break;
+          const int nst = __builtin_amdgcn_readfirstlane(step_list[si]);
+          const int sb2 = si % kStageBufs;
           const int64_t e0 = static_cast<int64_t>(sg.tok0(nst)) * p.hq + sg.h0(nst);  // first element row
           // clamp to the arrays (rows past the end are masked)
           const int lim_q = static_cast<int>(min<int64_t>(0x7fffffff, 2 * ((static_cast<int64_t>(n_q) * p.hq - e0) * D - 8)));
@@ -650,12 +654,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
           if (wave == 0)
             dma4_s(p.delta + e0, static_cast<uint32_t>(min(meta_off, lim_m) + plane_off), lds_addr(&smeta[sb2][0]));
         }
-        if (i < 0) continue;
+        if (jg < 0) continue;
 
+#pragma unroll 1
+        for (int q = 0; q < kStepsPerSync; ++q) {
+        const int i = jg * kStepsPerSync + q;
+        if (i >= cnt) break;
         // Per-lane constants are redefined opaquely every step so that the compiler
         // recomputes the few values derived from them instead of holding dozens.
         asm volatile("" : "+v"(f_q), "+v"(f_v), "+v"(t_a), "+v"(t_b), "+v"(rel));
-        const int sb = i % 3;
+        const int sb = i % kStageBufs;
         const int st = __builtin_amdgcn_readfirstlane(step_list[i]);
         const int tk = sg.tok0(st);
         const int rmax = sg.rows(st, n_q, grp);
@@ -771,6 +779,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+        }  // steps of the group
       }
       __syncthreads();  // all waves are done with the list and the stages
     }
