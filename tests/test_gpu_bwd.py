@@ -32,14 +32,14 @@ def gpu_fwd_merged(meta, inp, scale, dm):
     return o, lse
 
 
-def run_case(meta, inp, scale, gs, gl, tol, dq_init=None):
+def run_case(meta, inp, scale, gs, gl, tol, dq_init=None, workspace="auto"):
     dm = device_meta(meta, gs, gl)
     o, lse = gpu_fwd_merged(meta, inp, scale, dm)
     dq = torch.zeros(inp.q.shape, dtype=torch.float32, device="cuda") if dq_init is None \
         else dq_init.clone()
     dk, dv, dks, dvs = sxattn.sparse_xattn_bwd(dev(inp.q), dev(inp.k), dev(inp.v), dm, scale, o,
                                                dev(inp.dout), lse, dq, dev(inp.k_self),
-                                               dev(inp.v_self))
+                                               dev(inp.v_self), workspace=workspace)
     torch.cuda.synchronize()
     r = oracle.sparse_xattn_bwd(inp.q.f64, inp.k.f64, inp.v.f64, host64(o), inp.dout.f64,
                                 host64(lse), meta.anchor, meta.sample_start, gs, gl, scale,
@@ -81,11 +81,15 @@ def test_bwd_bf16_sharp_ragged_chunks_and_dq_accumulation(seed):
 
 
 def test_bwd_bf16_gqa_and_head_dim_variants():
-    for hq, hkv, d in [(4, 4, 64), (8, 4, 128), (16, 2, 128), (4, 2, 64)]:
+    """Group sizes 1, 2, 8 divide the 32-row query step; 3 does not (steps of 10
+    tokens with 2 padding rows); 40 exceeds it (a token's heads span two steps)."""
+    for hq, hkv, d in [(4, 4, 64), (8, 4, 128), (16, 2, 128), (4, 2, 64), (6, 2, 128), (3, 1, 64),
+                       (40, 1, 64)]:
         meta = synth.draw_meta(8, 3000, 300, 1200, 12)
         gs, gl = synth.contiguous_chunks(3000, 700)
         inp = synth.draw_inputs(8, meta, hq, hkv, d, "bf16", 1.0, gs, gl, with_dout=True)
-        run_case(meta, inp, 1.0 / math.sqrt(d), gs, gl, 3e-2)
+        for ws in ("auto", None):  # load-balanced dK/dV, and one workgroup per key tile
+            run_case(meta, inp, 1.0 / math.sqrt(d), gs, gl, 3e-2, workspace=ws)
 
 
 def test_bwd_fp32_tiny():

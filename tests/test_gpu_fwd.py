@@ -282,9 +282,9 @@ def test_fwd_only_self_and_empty_calls():
 
 
 def test_fwd_tiny_bf16_d64_and_gqa_variants():
-    """d = 64 and group sizes 1, 2, 8 (rows of a wave span several blocks or a
-    block spans several waves)."""
-    for hq, hkv, d in [(4, 4, 64), (8, 4, 128), (16, 2, 128), (4, 2, 64)]:
+    """d = 64 and group sizes 1, 2, 3, 8, 40 (rows of a wave span several blocks, a
+    block spans several waves, or a token's heads span several waves)."""
+    for hq, hkv, d in [(4, 4, 64), (8, 4, 128), (16, 2, 128), (4, 2, 64), (6, 2, 128), (40, 1, 64)]:
         meta = synth.draw_meta(7, 3000, 300, 1200, 12)
         gs, gl = synth.contiguous_chunks(3000, 700)
         inp = synth.draw_inputs(7, meta, hq, hkv, d, "bf16", 1.0, gs, gl)
