@@ -299,13 +299,13 @@ constexpr int kListCap = 2 * 64 * kKvWaves;  // step indices held in LDS at once
 // Stream-K list units: a tile with hits occupies kSetupUnits + hits consecutive units
 // of the per-head list (the first ones stand for its setup and write-back, so that a
 // share that starts many short tiles gets fewer steps); a tile without hits, none.
-constexpr int kSetupUnits = 5;
+constexpr int kSetupUnits = 7;
 
 struct DkdvSched {
   int32_t n_ctx_tiles, n_tiles;
   int32_t n_shares;        // stream-K workgroups; 0: one workgroup per (tile, kv head)
   const int32_t* prefix;   // [n_tiles + 1]: first list unit of each tile (per kv head)
-  const int4* tinfo;       // [n_tiles]: key-coordinate range (x, y) and hit steps (z) of each tile
+  const int4* tinfo;       // [n_tiles]: key-coordinate range (x, y), hit steps (z) and first hit step (w)
   const int32_t* coord;    // [n_loc]: global key coordinate of each local context row
   float* slots;            // [2 n_shares][kKeysPerWG][2][D]: partial dK, dV
 };
@@ -387,12 +387,22 @@ __global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched 
   __syncthreads();
   kmin = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
   kmax = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
-  int n = 0;
-  for (int base = 0; base < sg.n_steps; base += 256)
-    n += __syncthreads_count(step_hit(p, sg, base + tid, n_q, self_tile, kmin, kmax));
+  int n = 0, first = sg.n_steps;
+  for (int base = 0; base < sg.n_steps; base += 256) {
+    const bool hit = step_hit(p, sg, base + tid, n_q, self_tile, kmin, kmax);
+    const int cnt = __syncthreads_count(hit);
+    if (cnt > 0 && first == sg.n_steps) {  // first hit of this batch: smallest hitting thread
+      const uint64_t m = __ballot(hit);
+      if (tid % 64 == 0) red[0][wave] = m ? base + 64 * wave + __builtin_ctzll(m) : 0x7fffffff;
+      __syncthreads();
+      first = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
+      __syncthreads();
+    }
+    n += cnt;
+  }
   if (tid == 0) {
     prefix[t + 1] = n > 0 ? n + kSetupUnits : 0;
-    tinfo[t] = int4{kmin, kmax, n, 0};
+    tinfo[t] = int4{kmin, kmax, n, first};
     if (t == 0) prefix[0] = 0;
   }
 }
@@ -464,19 +474,32 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
   };
 
   bool first_seg = true;  // no segment with steps yet in this share
+  // (head, tile) holding list unit `pos`: a binary search for the share's first unit;
+  // later segments are the following tiles, so the walk below only steps forward
+  int g = 0, t = 0;
+  if (streamk && pos < end) {
+    g = static_cast<int>(pos / W);
+    const int r = static_cast<int>(pos % W);
+    int lo = 0, hi = sc.n_tiles;  // prefix[lo] <= r < prefix[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ld_uniform(sc.prefix, mid) <= r) lo = mid;
+      else hi = mid;
+    }
+    t = lo;
+  }
   while (pos < end) {
-    int g, t, s0, s1, hits = 0;
+    int s0, s1, hits = 0;
     int kmin, kmax;
+    int scan0 = 0;  // no step before this one hits the tile
     if (streamk) {
-      g = static_cast<int>(pos / W);
-      const int r = static_cast<int>(pos % W);
-      int lo = 0, hi = sc.n_tiles;  // prefix[lo] <= r < prefix[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (ld_uniform(sc.prefix, mid) <= r) lo = mid;
-        else hi = mid;
+      int r = static_cast<int>(pos - static_cast<int64_t>(g) * W);
+      if (r >= W) {  // next kv head
+        ++g;
+        r -= static_cast<int>(W);
+        t = 0;
       }
-      t = lo;
+      while (ld_uniform(sc.prefix, t + 1) <= r) ++t;  // skip tiles that end at or before r
       const int u0 = ld_uniform(sc.prefix, t) + kSetupUnits, u1 = ld_uniform(sc.prefix, t + 1);
       const int ue = static_cast<int>(min<int64_t>(u1, r + (end - pos)));  // end of this share in the tile
       pos += ue - r;
@@ -485,6 +508,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
       kmin = __builtin_amdgcn_readfirstlane(ti.x);
       kmax = __builtin_amdgcn_readfirstlane(ti.y);
       hits = __builtin_amdgcn_readfirstlane(ti.z);
+      scan0 = __builtin_amdgcn_readfirstlane(ti.w);
       s0 = max(r, u0) - u0;
       s1 = ue - u0;
     } else {
@@ -508,7 +532,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
       kvalid[hh] = krow0 + krow[hh] < key_rows;
       krc[hh] = kvalid[hh] ? krow0 + krow[hh] : key_rows - 1;
     }
-    __syncthreads();  // the previous segment is done with vtile, red, the list and the stages
+    // The previous segment's pipeline ended with a barrier after its last read of
+    // vtile, the list and the stages; this one only orders `red` (tile mode) and lets
+    // the previous write-back stay in flight while this segment's copies start.
+    lds_barrier();
     {  // V rows of the tile -> LDS (direct copies into the swizzled layout)
       const uint16_t* V = self_tile ? p.v_self : p.v;
       constexpr int VI = kKeysPerWG * CPR / kT;  // copies per lane
@@ -541,7 +568,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
         red[0][wave] = kmin;
         red[1][wave] = kmax;
       }
-      __syncthreads();
+      lds_barrier();
       kmin = red[0][0];
       kmax = red[1][0];
 #pragma unroll
@@ -591,8 +618,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
     int t_b = LdsTile<D>::tr_off(8 + 4 * h2 + ((lane & 15) >> 2), (lane >> 4) & 1, lane & 15);
     int rel = 4 * h2;  // step row of accumulator row 4 j + i: 8 j + rel + i
 
-    int scan = 0;  // next step to examine
-    int ord = 0;   // hits of this tile before `scan`
+    int scan = scan0;  // next step to examine
+    int ord = 0;       // hits of this tile before `scan`
     while (scan < sg.n_steps && ord < s1) {
       // ---- collect the step indices of hits ord in [s0, s1), up to the list capacity
       int cnt = 0;
@@ -601,7 +628,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
         const bool hit = step_hit(p, sg, st, n_q, self_tile, kmin, kmax);
         const uint64_t m = __ballot(hit);
         if (lane == 0) wave_cnt[wave] = __popcll(m);
-        __syncthreads();
+        lds_barrier();
         int pre = 0, tot = 0;
 #pragma unroll
         for (int w2 = 0; w2 < kWaves; ++w2) {
@@ -622,7 +649,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
         cnt += max(0, min(ord + tot, s1) - first);
         ord += tot;
         scan += kT;
-        __syncthreads();
+        lds_barrier();
       }
 
       // ---- pipeline over the listed steps in groups of kStepsPerSync: iteration j

@@ -180,6 +180,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier that publishes this wave's LDS writes (lgkmcnt(0)) but does not
+// wait for vector-memory operations, so copies and stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier without a memory fence (the fence of __syncthreads would also
 // wait for every DMA still in flight).  LDS written by ds_write must be waited for
 // (lgkmcnt) by the writer before it.
