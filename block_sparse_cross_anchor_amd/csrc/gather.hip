@@ -12,6 +12,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
+constexpr int kPerThread = 4;  // 16-byte copies per thread, all loads issued before the stores
+
+// Workgroup (c, s) copies the s-th run of kThreads * kPerThread 16-byte units of chunk c.
 __global__ __launch_bounds__(kThreads) void gather_kernel(const uint8_t* __restrict__ src,
                                                           int64_t row_bytes,
                                                           const int32_t* __restrict__ cgs,
@@ -26,16 +29,16 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint8_t* __restr
   const u32x4* s = reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(cgs[c]) * row_bytes);
   u32x4* d = reinterpret_cast<u32x4*>(dst + off * row_bytes);
   const int64_t n16 = rows * row_bytes / 16;
-  const int64_t stride = static_cast<int64_t>(gridDim.y) * kThreads;
-  int64_t i = static_cast<int64_t>(blockIdx.y) * kThreads + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = s[i], b = s[i + stride], e = s[i + 2 * stride], f = s[i + 3 * stride];
-    d[i] = a;
-    d[i + stride] = b;
-    d[i + 2 * stride] = e;
-    d[i + 3 * stride] = f;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.y) * kThreads * kPerThread + threadIdx.x;
+  for (int64_t base = i0; base < n16; base += static_cast<int64_t>(gridDim.y) * kThreads * kPerThread) {
+    u32x4 v[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      if (base + j * kThreads < n16) v[j] = s[base + j * kThreads];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+      if (base + j * kThreads < n16) d[base + j * kThreads] = v[j];
   }
-  for (; i < n16; i += stride) d[i] = s[i];
 }
 
 }  // namespace
@@ -43,9 +46,10 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint8_t* __restr
 hipError_t launch_context_gather(const void* src, int64_t row_bytes, const int32_t* chunk_gstart,
                                  const int32_t* chunk_len, int32_t n_chunk, int64_t n_dst_rows,
                                  void* dst, hipStream_t s) {
-  const int64_t total16 = n_dst_rows * row_bytes / 16;
-  int64_t stripes = total16 / (static_cast<int64_t>(n_chunk) * kThreads * 8);
-  stripes = stripes < 1 ? 1 : (stripes > 256 ? 256 : stripes);
+  // runs per chunk: enough for the mean chunk length (longer chunks loop)
+  const int64_t per_chunk16 = (n_dst_rows + n_chunk - 1) / n_chunk * row_bytes / 16;
+  int64_t stripes = (per_chunk16 + kThreads * kPerThread - 1) / (kThreads * kPerThread);
+  stripes = stripes < 1 ? 1 : (stripes > 65535 ? 65535 : stripes);
   gather_kernel<<<dim3(static_cast<unsigned>(n_chunk), static_cast<unsigned>(stripes)), dim3(kThreads), 0,
                   s>>>(static_cast<const uint8_t*>(src), row_bytes, chunk_gstart, chunk_len, n_dst_rows,
                        static_cast<uint8_t*>(dst));
