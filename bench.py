@@ -25,6 +25,7 @@ bounded sample of blocks of the same workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -48,18 +49,32 @@ def log(*a):
 
 
 class Timers:
-    """HIP events around launches on the current stream, grouped by kernel name."""
+    """HIP events around launches on the current stream, grouped by kernel name.
+
+    Every event is created by `reserve` before the timed region: creating events
+    inside it can stall the host for tens of milliseconds once the runtime grows
+    its event pool, and the GPU would run dry meanwhile."""
 
     def __init__(self, torch):
         self.torch = torch
         self.pending = []
         self.enabled = False
+        self.calls = 0   # timed-call sites seen while disabled (one warmup step's worth)
+        self.pool = []
+
+    def reserve(self, n):
+        t = self.torch
+        self.pool = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True))
+                     for _ in range(n)]
+        self.pool.reverse()
 
     def run(self, name, work, fn):
         if not self.enabled:
+            self.calls += 1
             return fn()
-        t = self.torch
-        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        if not self.pool:
+            raise RuntimeError("Timers: more timed calls than reserved events")
+        e0, e1 = self.pool.pop()
         e0.record()
         out = fn()
         e1.record()
@@ -251,11 +266,13 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=5)  # at least 1
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    if args.warmup < 1 or args.steps < 1:
+        ap.error("--steps and --warmup must be at least 1")
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the context; --gpus {args.gpus} is not "
               "supported (the multi-device path is design only, see the design notes)",
@@ -275,17 +292,23 @@ def main():
     w = P["w"]
     T = Timers(torch)
     log(f"warmup {args.warmup} steps ...")
-    for _ in range(args.warmup):
+    step(torch, P, T)   # counts the timed call sites of one step
+    per_step, T.calls = T.calls, 0
+    for _ in range(args.warmup - 1):
         step(torch, P, T)
+    T.reserve(per_step * args.steps)
     torch.cuda.synchronize()
     T.enabled = True
     log(f"timing {args.steps} steps ...")
+    gc.collect()
+    gc.disable()   # no collector pause inside the timed region
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         bins, load, cost, bin_pairs = step(torch, P, T)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    gc.enable()
     ms_step = el * 1e3 / args.steps
     ctx_pairs = int(cost.sum())
     pairs = ctx_pairs + 16 * w.n_q
