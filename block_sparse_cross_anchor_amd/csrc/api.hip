@@ -60,6 +60,8 @@ int check_attn(const void* q, const void* k, const void* v, sxa_dtype in_dtype, 
     return fail(SXA_EINVAL, "query tensor too large");
   if (static_cast<int64_t>(n_blk) * sxa::kBlock * hq >= (int64_t{1} << 29))
     return fail(SXA_EUNSUPPORTED, "n_blk * 16 * hq must be below 2^29 query rows");
+  if (hkv > 4096)  // per-lane byte offsets of a key tile's rows are 24-bit products
+    return fail(SXA_EUNSUPPORTED, "hkv %d is above the supported 4096", hkv);
   if ((k_self == nullptr) != (v_self == nullptr))
     return fail(SXA_EINVAL, "k_self and v_self must be both NULL or both non-NULL");
   if (n_blk > 0 && (q == nullptr || anchor == nullptr || sample_start == nullptr))

@@ -90,7 +90,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int ROWS = 32 * kDqWaves;
-  using Dma = TileDma<D, kDqWaves>;
+  using Dma = TileDma<D, kDqWaves, false>;
   __shared__ __attribute__((aligned(256))) uint16_t bufs[3][Dma::ELEMS];
 
   const int tid = threadIdx.x;
@@ -161,16 +161,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
   // so that the only vector-memory operations in flight in the loop are the copies.
   wait_vmcnt<0>();
   Tile n1, n2;
-  Dma::issue(cur, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[0]);
+  const Dma dma(p.hkv, wave, lane);
+  dma.issue(cur, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[0]));
   bool have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
-  if (have1) Dma::issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[1]);
+  if (have1) dma.issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[1]));
   int cb = 0;
   while (true) {
     if (have1) wait_vmcnt<Dma::NI>();  // this wave's copies of `cur` landed (n1 may fly)
     else wait_vmcnt<0>();
     barrier_nofence();                 // ... and every wave's; all reads of the third buffer are done
     const bool have2 = have1 && walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);
-    if (have2) Dma::issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[cb == 0 ? 2 : cb - 1]);
+    if (have2) dma.issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[cb == 0 ? 2 : cb - 1]));
 
     // per-lane constants are redefined opaquely per tile so that derived addresses
     // are recomputed rather than held

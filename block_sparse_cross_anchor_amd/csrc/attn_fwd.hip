@@ -75,7 +75,7 @@ fwd_bf16_kernel(FwdParams p) {
   constexpr int ROWS = 32 * NT * WAVES;  // rows per workgroup
   constexpr int KS = D / 16;             // k-steps of S^T
   constexpr int DT = D / 32;             // 32-row d tiles of O^T
-  using Dma = TileDma<D, WAVES>;
+  using Dma = TileDma<D, WAVES, true>;
   __shared__ __attribute__((aligned(256))) uint16_t bufs[NSTAGE][Dma::ELEMS];
 
   const int tid = threadIdx.x;
@@ -168,11 +168,12 @@ fwd_bf16_kernel(FwdParams p) {
   int t_b = LdsTile<D>::tr_off(8 + 4 * h2 + ((lane & 15) >> 2), (lane >> 4) & 1, lane & 15);
   constexpr uint32_t kVOff = kTileKeys * D * 2;  // V rows follow the K rows
   Tile n1, n2;
-  Dma::issue(cur, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[0]);
+  const Dma dma(p.hkv, wave, lane);
+  dma.issue(cur, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[0]));
   bool have1 = false;
   if constexpr (NSTAGE == 3) {
     have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
-    if (have1) Dma::issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[1]);
+    if (have1) dma.issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[1]));
   }
   int cb = 0;
   while (true) {
@@ -182,12 +183,12 @@ fwd_bf16_kernel(FwdParams p) {
       else wait_vmcnt<0>();
       barrier_nofence();                 // ... and every wave's; all reads of the third buffer are done
       have2 = have1 && walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);
-      if (have2) Dma::issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[cb == 0 ? 2 : cb - 1]);
+      if (have2) dma.issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[cb == 0 ? 2 : cb - 1]));
     } else {
       wait_vmcnt<0>();
       barrier_nofence();  // `cur` landed everywhere; the other buffer is no longer read
       have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
-      if (have1) Dma::issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, wave, lane, bufs[cb ^ 1]);
+      if (have1) dma.issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[cb ^ 1]));
     }
       // per-lane constants are redefined opaquely per tile so that derived addresses
       // are recomputed rather than held

@@ -83,31 +83,68 @@ __device__ __forceinline__ bool walk_next(Walk& w, const int32_t* __restrict__ c
 // writes the 16 bytes at LDS offset 16 i of its 1 KiB slice, so each lane picks the
 // global chunk that belongs at that position under the swizzle.  Rows past the tile
 // end repeat its last row (those keys are masked; any finite value will do).  Every
-// wave issues NI copies per tile.
-template <int D, int WAVES>
+// wave issues NI copies per tile.  The address is the tile's first element (uniform,
+// in scalar registers) plus a 32-bit per-lane byte offset.  With KEEP the offsets
+// of a full tile (the same for every tile) are computed once and held in registers;
+// without, they are recomputed per tile (a kernel with no registers to spare).
+template <int D, int WAVES, bool KEEP>
 struct TileDma {
   static constexpr int CPR = D / 8;
   static constexpr int HALF = kTileKeys * CPR;  // chunks of K (or V) per tile
   static constexpr int NI = 2 * HALF / 64 / WAVES;
   static_assert(NI * 64 * WAVES == 2 * HALF, "tile must split evenly over the waves");
+  static_assert(HALF % 64 == 0, "an instruction copies K or V, never both");
   static constexpr int ELEMS = 2 * kTileKeys * D;  // bf16 per buffer
 
-  __device__ static __forceinline__ void issue(const Tile& t, const uint16_t* k, const uint16_t* v,
-                                               const uint16_t* k_self, const uint16_t* v_self, int hkv,
-                                               int g, int wave, int lane, uint16_t* buf) {
+  int w;            // wave index (uniform)
+  uint32_t stride;  // bytes per source row: hkv * D * 2 (< 2^24, so 24-bit products suffice)
+  uint32_t voff[KEEP ? NI : 1];
+
+  // chunk `cc` of K or V: its row in the tile and the byte offset of its 16 bytes
+  // inside that row under the swizzle
+  __device__ static __forceinline__ uint32_t row_of(uint32_t cc) { return cc / CPR; }
+  __device__ static __forceinline__ uint32_t col_bytes(uint32_t cc) {
+    return 16 * ((cc % CPR) ^ LdsTile<D>::swz(static_cast<int>(cc / CPR)));
+  }
+  __device__ static __forceinline__ uint32_t chunk(int inst, int lane) {
+    return static_cast<uint32_t>(inst * 64 - (inst * 64 >= HALF ? HALF : 0) + lane);
+  }
+
+  __device__ __forceinline__ TileDma(int hkv, int wave, int lane) {
+    w = __builtin_amdgcn_readfirstlane(wave);
+    stride = static_cast<uint32_t>(hkv) * D * 2;
+#pragma unroll
+    for (int j = 0; j < (KEEP ? NI : 1); ++j) {
+      const uint32_t cc = chunk(w * NI + j, lane);
+      voff[j] = __umul24(row_of(cc), stride) + col_bytes(cc);
+    }
+  }
+
+  // lds: byte address of the tile buffer in LDS
+  __device__ __forceinline__ void issue(const Tile& t, const uint16_t* k, const uint16_t* v,
+                                        const uint16_t* k_self, const uint16_t* v_self, int hkv, int g,
+                                        int lane, uint32_t lds) const {
     const uint16_t* K = t.self ? k_self : k;
     const uint16_t* V = t.self ? v_self : v;
-    const int last = t.nrows - 1;
+    const int64_t first = (t.row0 * hkv + g) * D;  // element offset of the tile's row 0
+    const uint32_t lb = lds + static_cast<uint32_t>(w * NI * 1024);
+    if (KEEP && t.nrows == kTileKeys) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int inst = wave * NI + j;
-      const int c = inst * 64 + lane;
-      const bool isv = c >= HALF;  // uniform per instruction
-      const int cc = isv ? c - HALF : c;
-      const int row = cc / CPR;
-      const int logical = (cc % CPR) ^ LdsTile<D>::swz(row);
-      const uint16_t* src = (isv ? V : K) + ((t.row0 + min(row, last)) * hkv + g) * D + 8 * logical;
-      dma16(src, lds_addr(buf + inst * 512));
+      for (int j = 0; j < NI; ++j) {
+        const bool isv = (w * NI + j) * 64 >= HALF;  // uniform per instruction
+        dma16_s((isv ? V : K) + first, voff[j], lb + 1024 * j);
+      }
+    } else {
+      const uint32_t last = static_cast<uint32_t>(t.nrows - 1);
+      int ln = lane;
+      asm volatile("" : "+v"(ln));  // recomputed here, not hoisted into held registers
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const bool isv = (w * NI + j) * 64 >= HALF;
+        const uint32_t cc = chunk(w * NI + j, ln);
+        const uint32_t o = __umul24(min(row_of(cc), last), stride) + col_bytes(cc);
+        dma16_s((isv ? V : K) + first, o, lb + 1024 * j);
+      }
     }
   }
 };

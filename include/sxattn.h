@@ -78,6 +78,7 @@ typedef enum {
  * statistics).
  *   q [n_q][hq][d], k/v [n_loc][hkv][d] in in_dtype; d in {64, 128}; block_size == 16;
  *   hq % hkv == 0.  n_chunk >= 0 (0 with k_self set gives the own-block partial alone).
+ *   Size limits (SXA_EUNSUPPORTED beyond them): n_blk * 16 * hq < 2^29, hkv <= 4096.
  *   o [n_q][hq][d] in o_dtype (SXA_F32 or SXA_BF16; SXA_F32 input requires SXA_F32 output),
  *   lse [n_q][hq] float32.  Both are overwritten.
  *   workspace, workspace_bytes: optional device scratch (at least
