@@ -7,19 +7,21 @@ tokens and planned onto 8 virtual devices ("bins"):
 
   1. chunk_cost   realised cost of each chunk (GPU, int64), copied to the host
   2. lpt_assign   longest-processing-time-first plan with equal chunk counts (host)
-  3. context_gather  each bin's chunks of K and V into its local buffer
-  4. sparse_xattn_fwd per bin (the own-block term on bin 0): partial O, lse
-  5. lse_combine  of the 8 partials
-  6. sparse_xattn_bwd: delta pre-pass, then per bin the dQ phase (accumulated)
-     and the dK/dV phase
+  3. per bin: context_gather of its chunks of K and V into its local buffer, then
+     sparse_xattn_fwd (the own-block term on bin 0): partial O, lse
+  4. lse_combine  of the 8 partials
+  5. sparse_xattn_bwd: delta pre-pass, then the dQ phase of every bin (accumulated)
+     and the dK/dV phase of every bin
 
 Throughput is useful attention FLOP/s: 4*d*Hq FLOP per allowed (query, key) pair
 for the forward and 10*d*Hq for the backward, over the allowed pairs only
 (context pairs from the cost kernel plus 16 own-block pairs per query).
 
-Prints one JSON line.  HIP events around every launch give the per-kernel
-durations for the roofline of the dominant kernel; the CPU oracle is timed on a
-bounded sample of blocks of the same workload.
+Prints one JSON line.  The timed steps carry HIP events only around the dominant
+phase (one pair per step around its 8 launches): recording an event costs GPU time,
+so events around every launch would slow the step they measure.  The per-phase
+breakdown comes from the warm-up steps, which carry events around every phase.  The
+CPU oracle is timed on a bounded sample of blocks of the same workload.
 """
 
 from __future__ import annotations
@@ -49,17 +51,18 @@ def log(*a):
 
 
 class Timers:
-    """HIP events around launches on the current stream, grouped by kernel name.
+    """HIP events around phases on the current stream, grouped by phase name.
 
-    Every event is created by `reserve` before the timed region: creating events
-    inside it can stall the host for tens of milliseconds once the runtime grows
-    its event pool, and the GPU would run dry meanwhile."""
+    `only` selects the phases that get events: None (none), "all", or one name.
+    Events are created by `reserve` before they are recorded: creating them inside
+    a timed region can stall the host for tens of milliseconds once the runtime
+    grows its event pool, and the GPU would run dry meanwhile."""
 
     def __init__(self, torch):
         self.torch = torch
         self.pending = []
-        self.enabled = False
-        self.calls = 0   # timed-call sites seen while disabled (one warmup step's worth)
+        self.only = None
+        self.calls = {}   # phase name -> calls seen while counting
         self.pool = []
 
     def reserve(self, n):
@@ -68,27 +71,30 @@ class Timers:
                      for _ in range(n)]
         self.pool.reverse()
 
-    def run(self, name, work, fn):
-        if not self.enabled:
-            self.calls += 1
+    def run(self, name, work, fn, launches=1):
+        if self.only is None:
+            self.calls[name] = self.calls.get(name, 0) + 1
+            return fn()
+        if self.only != "all" and self.only != name:
             return fn()
         if not self.pool:
-            raise RuntimeError("Timers: more timed calls than reserved events")
+            raise RuntimeError("Timers: more timed phases than reserved events")
         e0, e1 = self.pool.pop()
         e0.record()
         out = fn()
         e1.record()
-        self.pending.append((name, work, e0, e1))
+        self.pending.append((name, work, launches, e0, e1))
         return out
 
     def summary(self):
         agg = {}
-        for name, work, e0, e1 in self.pending:
+        for name, work, launches, e0, e1 in self.pending:
             ms = e0.elapsed_time(e1)
-            a = agg.setdefault(name, {"ms": 0.0, "launches": 0, "work": 0.0})
+            a = agg.setdefault(name, {"ms": 0.0, "launches": 0, "work": 0.0, "calls": 0})
             a["ms"] += ms
-            a["launches"] += 1
+            a["launches"] += launches
             a["work"] += work
+            a["calls"] += 1
         return agg
 
 
@@ -169,7 +175,6 @@ def step(torch, P, T):
         m.anchor, m.sample_start, m.chunk_gstart, m.chunk_len = P["anchor"], P["start"], gsb, glb
         m.n_blk, m.n_chunk, m.n_loc = w.n_anchor, per_bin, n_loc
         metas.append(m)
-    for b in range(nb):
         pairs = bin_pairs[b] + (self_pairs if b == 0 else 0)
         T.run("sparse_xattn_fwd", 4.0 * d * hq * pairs,
               lambda b=b: sxattn.sparse_xattn_fwd(
@@ -187,20 +192,21 @@ def step(torch, P, T):
                                           P["do"], lse, P["dq"], delta_ws=P["delta"],
                                           dk=P["dk_loc"][0], dv=P["dv_loc"][0],
                                           flags=sxattn.BWD_DELTA))
-    for b in range(nb):
-        pairs = bin_pairs[b] + (self_pairs if b == 0 else 0)
+    all_pairs = sum(bin_pairs) + self_pairs
+
+    def bwd(b, flags):
         self_kv = (P["ks"], P["vs"]) if b == 0 else (None, None)
-        flags = sxattn.BWD_DQ | (sxattn.BWD_DQ_OVERWRITE if b == 0 else 0)
-        T.run("bwd_dq", 6.0 * d * hq * pairs,
-              lambda b=b, self_kv=self_kv, flags=flags: sxattn.sparse_xattn_bwd(
-                  P["q"], P["k_loc"][b], P["v_loc"][b], metas[b], scale, o, P["do"], lse, P["dq"],
-                  self_kv[0], self_kv[1], delta_ws=P["delta"], dk=P["dk_loc"][b],
-                  dv=P["dv_loc"][b], dk_self=P["dks"], dv_self=P["dvs"], flags=flags))
-        T.run("bwd_dkdv", 8.0 * d * hq * pairs,
-              lambda b=b, self_kv=self_kv: sxattn.sparse_xattn_bwd(
-                  P["q"], P["k_loc"][b], P["v_loc"][b], metas[b], scale, o, P["do"], lse, P["dq"],
-                  self_kv[0], self_kv[1], delta_ws=P["delta"], dk=P["dk_loc"][b],
-                  dv=P["dv_loc"][b], dk_self=P["dks"], dv_self=P["dvs"], flags=sxattn.BWD_DKDV))
+        sxattn.sparse_xattn_bwd(
+            P["q"], P["k_loc"][b], P["v_loc"][b], metas[b], scale, o, P["do"], lse, P["dq"],
+            self_kv[0], self_kv[1], delta_ws=P["delta"], dk=P["dk_loc"][b], dv=P["dv_loc"][b],
+            dk_self=P["dks"], dv_self=P["dvs"], flags=flags)
+
+    # each phase as one group of nb launches (bin 0 overwrites dQ, the others add)
+    T.run("bwd_dq", 6.0 * d * hq * all_pairs,
+          lambda: [bwd(b, sxattn.BWD_DQ | (sxattn.BWD_DQ_OVERWRITE if b == 0 else 0)) for b in range(nb)],
+          launches=nb)
+    T.run("bwd_dkdv", 8.0 * d * hq * all_pairs,
+          lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)], launches=nb)
     return bins_np, load.numpy(), cost_np, bin_pairs
 
 
@@ -292,13 +298,23 @@ def main():
     w = P["w"]
     T = Timers(torch)
     log(f"warmup {args.warmup} steps ...")
-    step(torch, P, T)   # counts the timed call sites of one step
-    per_step, T.calls = T.calls, 0
-    for _ in range(args.warmup - 1):
-        step(torch, P, T)
-    T.reserve(per_step * args.steps)
-    torch.cuda.synchronize()
-    T.enabled = True
+    step(torch, P, T)   # counts the timed phases of one step
+    per_step = dict(T.calls)
+    if args.warmup > 1:   # the other warm-up steps give the per-phase breakdown
+        T.reserve(sum(per_step.values()) * (args.warmup - 1))
+        T.only = "all"
+        for _ in range(args.warmup - 1):
+            step(torch, P, T)
+        torch.cuda.synchronize()
+        per_kernel = T.summary()
+        T.pending = []
+    else:
+        per_kernel = {}
+    # the dominant phase: the most time per step in the breakdown (the backward's
+    # dK/dV phase when there is no breakdown)
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["ms"]) if per_kernel else "bwd_dkdv"
+    T.reserve(per_step[dom] * args.steps)
+    T.only = dom
     log(f"timing {args.steps} steps ...")
     gc.collect()
     gc.disable()   # no collector pause inside the timed region
@@ -314,10 +330,7 @@ def main():
     pairs = ctx_pairs + 16 * w.n_q
     flop = 14.0 * w.d * w.hq * pairs
     value = flop / (ms_step * 1e-3) / 1e12
-    per_kernel = T.summary()
-    breakdown = {n: round(a["ms"] / args.steps, 4) for n, a in per_kernel.items()}
-    dom = max(per_kernel, key=lambda n: per_kernel[n]["ms"])
-    a = per_kernel[dom]
+    a = T.summary()[dom]
     avg_ms = a["ms"] / a["launches"]
     work_per_launch = a["work"] / a["launches"]
     is_mfma = dom in ("sparse_xattn_fwd", "bwd_dq", "bwd_dkdv")
@@ -327,11 +340,12 @@ def main():
                 "peak": peak, "unit": "TFLOP/s" if is_mfma else "GB/s",
                 "frac": round(achieved / peak, 4), "traffic": recorded_traffic(dom), "kernel": dom,
                 "avg_launch_ms": round(avg_ms, 4), "launches_per_step": a["launches"] // args.steps}
-    kernels = {}
+    kernels = {}   # from the warm-up steps with events around every phase
+    n_bd = max(args.warmup - 1, 1)
     for n, k in per_kernel.items():
         mf = n in ("sparse_xattn_fwd", "bwd_dq", "bwd_dkdv")
         rate = k["work"] / (k["ms"] * 1e-3) / (1e12 if mf else 1e9)
-        kernels[n] = {"ms_per_step": round(k["ms"] / args.steps, 4),
+        kernels[n] = {"ms_per_step": round(k["ms"] / n_bd, 4),
                       ("TFLOP/s" if mf else "GB/s"): round(rate, 1)}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -346,6 +360,7 @@ def main():
                    "lpt_imbalance": round(float(load.max() / load.mean() - 1), 5)},
         "roofline": roofline,
         "kernels": kernels,
+        "kernels_note": f"per-phase times from {n_bd} warm-up steps with events around every phase",
     }
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")

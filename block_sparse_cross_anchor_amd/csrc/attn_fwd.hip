@@ -45,6 +45,10 @@ namespace sxa {
 namespace {
 
 constexpr float kRescaleSlack = 8.f;  // log2 units
+#ifndef SXA_FWD_KPF
+#define SXA_FWD_KPF 1
+#endif
+constexpr int KPF = SXA_FWD_KPF;  // k-steps between a K fragment's LDS read and its MFMA
 
 
 struct FwdParams {
@@ -216,15 +220,27 @@ fwd_bf16_kernel(FwdParams p) {
           for (int nt = 0; nt < NT; ++nt)
   #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[mt][nt][r] = 0.f;
+        // K fragments are read KPF k-steps ahead of their MFMAs, so the LDS latency
+        // is covered by the MFMAs in between
+        bf16x8 kf[KPF + 1][2];
+  #pragma unroll
+        for (int ks = 0; ks < KPF; ++ks)
+  #pragma unroll
+          for (int mt = 0; mt < 2; ++mt) kf[ks][mt] = lds_frag((kb ^ (32 * ks)) + mt * 64 * D);
   #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
+          if (ks + KPF < KS) {
   #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 kf = lds_frag((kb ^ (32 * ks)) + mt * 64 * D);
+            for (int mt = 0; mt < 2; ++mt)
+              kf[(ks + KPF) % (KPF + 1)][mt] = lds_frag((kb ^ (32 * (ks + KPF))) + mt * 64 * D);
+          }
+  #pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
   #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-              sacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], sacc[mt][nt], 0, 0, 0);
-          }
+              sacc[mt][nt] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % (KPF + 1)][mt], qf[nt][ks], sacc[mt][nt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         bf16x8 pf[NT][4];
         bool need[NT];
@@ -233,12 +249,15 @@ fwd_bf16_kernel(FwdParams p) {
   #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           if (!all_full) {
+            // key = c + 4 h2 with c a compile-time constant: compare c against the
+            // bounds shifted by 4 h2, so no per-element key is held in a register
+            const int lo = a_lo[nt] - 4 * h2, hi = a_hi[nt] - 4 * h2;
   #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
   #pragma unroll
               for (int r = 0; r < 16; ++r) {
-                const int key = 32 * mt + 8 * (r / 4) + 4 * h2 + (r % 4);
-                if (key < a_lo[nt] || key >= a_hi[nt]) sacc[mt][nt][r] = -INFINITY;
+                const int c = 32 * mt + 8 * (r / 4) + (r % 4);
+                if (c < lo || c >= hi) sacc[mt][nt][r] = -INFINITY;
               }
           }
           float mx = -INFINITY;
@@ -344,7 +363,10 @@ fwd_bf16_kernel(FwdParams p) {
 #ifndef SXA_FWD_STAGES
 #define SXA_FWD_STAGES 3
 #endif
-constexpr int kNT = 1;                  // 32 query rows per wave
+#ifndef SXA_FWD_NT
+#define SXA_FWD_NT 1
+#endif
+constexpr int kNT = SXA_FWD_NT;         // 32-row query tiles per wave
 constexpr int kWaves = SXA_FWD_WAVES;   // waves sharing each K/V tile
 constexpr int kStages = SXA_FWD_STAGES; // K/V tile buffers
 constexpr int kRowsPerWG = 32 * kNT * kWaves;
