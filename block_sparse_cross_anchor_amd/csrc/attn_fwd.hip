@@ -75,7 +75,6 @@ template <int D, int NT, int WAVES, int NSTAGE, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES))) void
 fwd_bf16_kernel(FwdParams p) {
   static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three tile buffers");
-  constexpr int T = 64 * WAVES;
   constexpr int ROWS = 32 * NT * WAVES;  // rows per workgroup
   constexpr int KS = D / 16;             // k-steps of S^T
   constexpr int DT = D / 32;             // 32-row d tiles of O^T
@@ -113,7 +112,7 @@ fwd_bf16_kernel(FwdParams p) {
       for (int r = 0; r < 16; ++r) oacc[dt][nt][r] = 0.f;
   }
 
-  Tile cur, nxt;
+  Tile cur;
   const bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
   if (!have) {  // no allowed key in this call: O = 0, lse = -inf
 #pragma unroll
