@@ -170,7 +170,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
     if (have1) wait_vmcnt<Dma::NI>();  // this wave's copies of `cur` landed (n1 may fly)
     else wait_vmcnt<0>();
     barrier_nofence();                 // ... and every wave's; all reads of the third buffer are done
-    const bool have2 = have1 && walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);
+    const bool have2 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);  // false once exhausted
     if (have2) dma.issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[cb == 0 ? 2 : cb - 1]));
 
     // per-lane constants are redefined opaquely per tile so that derived addresses

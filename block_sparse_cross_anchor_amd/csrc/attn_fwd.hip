@@ -185,7 +185,7 @@ fwd_bf16_kernel(FwdParams p) {
       if (have1) wait_vmcnt<Dma::NI>();  // this wave's DMA of `cur` done (n1 may be in flight)
       else wait_vmcnt<0>();
       barrier_nofence();                 // ... and every wave's; all reads of the third buffer are done
-      have2 = have1 && walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);
+      have2 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);  // false once exhausted
       if (have2) dma.issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[cb == 0 ? 2 : cb - 1]));
     } else {
       wait_vmcnt<0>();

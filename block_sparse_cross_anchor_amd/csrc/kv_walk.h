@@ -20,62 +20,67 @@ struct Tile {
   int self;      // 1: own-block tile
 };
 
-// Position in the sequence of tiles of one workgroup (uniform across it).
+// Position in the sequence of tiles of one workgroup (uniform across it).  The
+// own-block rows form the first run of tiles, then each chunk that meets the
+// interval.  The next tile of the current run is held ready (source row, key
+// coordinate, tiles left in the run, rows from it to the run's end), so a step is a
+// handful of scalar operations with no branch; only a change of run branches.
+// Once exhausted, walk_next keeps returning false.
 struct Walk {
-  int self_pos, self_end;
-  int c;
-  int64_t off;
-  int gs, len, t, t_end;
+  int nc;         // next chunk to examine
+  int64_t off;    // local row of chunk nc
+  int64_t row;    // next tile: source row
+  int coord;      //            key coordinate
+  int left;       //            tiles left in its run, itself included
+  int rows_left;  //            rows from it to its run's end
+  int self;       //            1: own-block run
 
   __device__ void start(bool with_self, int b_first, int b_last) {
-    self_pos = with_self ? 16 * b_first : 0;
-    self_end = with_self ? 16 * (b_last + 1) : 0;
-    c = -1;
+    nc = 0;
     off = 0;
-    gs = len = t = t_end = 0;
+    row = with_self ? 16 * b_first : 0;
+    coord = static_cast<int>(row);
+    rows_left = with_self ? 16 * (b_last - b_first + 1) : 0;
+    left = (rows_left + kTileKeys - 1) / kTileKeys;
+    self = 1;
   }
 };
 
 __device__ __forceinline__ bool walk_next(Walk& w, const int32_t* __restrict__ cgs,
                                           const int32_t* __restrict__ clen, int n_chunk, int LO,
                                           int HI, Tile& out) {
-  if (w.self_pos < w.self_end) {
-    out.row0 = w.self_pos;
-    out.nrows = min(kTileKeys, w.self_end - w.self_pos);
-    out.coord0 = w.self_pos;
-    out.self = 1;
-    w.self_pos += kTileKeys;
-    return true;
-  }
-  while (true) {
-    if (w.t < w.t_end) {
-      out.row0 = w.off + static_cast<int64_t>(w.t) * kTileKeys;
-      out.nrows = min(kTileKeys, w.len - w.t * kTileKeys);
-      out.coord0 = w.gs + w.t * kTileKeys;
-      out.self = 0;
-      ++w.t;
-      return true;
-    }
-    if (w.c >= n_chunk) return false;
-    w.off += w.len;
-    ++w.c;
-    if (w.c >= n_chunk) {
-      w.len = 0;
-      return false;
-    }
-    // uniform index + constant address space: scalar loads, counted apart from
-    // the vector-memory queue that the tile copies use
-    const int c = __builtin_amdgcn_readfirstlane(w.c);
-    w.gs = ((const __attribute__((address_space(4))) int32_t*)(cgs))[c];
-    w.len = ((const __attribute__((address_space(4))) int32_t*)(clen))[c];
-    const int a = max(LO, w.gs), e = min(HI, w.gs + w.len);
-    if (a < e) {
-      w.t = (a - w.gs) / kTileKeys;
-      w.t_end = (e - w.gs + kTileKeys - 1) / kTileKeys;
-    } else {
-      w.t = w.t_end = 0;
+  if (__builtin_expect(w.left == 0, 0)) {  // next chunk that meets [LO, HI)
+    while (true) {
+      if (w.nc >= n_chunk) return false;
+      // uniform index + constant address space: scalar loads, counted apart from
+      // the vector-memory queue that the tile copies use
+      const int c = __builtin_amdgcn_readfirstlane(w.nc);
+      const int gs = ((const __attribute__((address_space(4))) int32_t*)(cgs))[c];
+      const int len = ((const __attribute__((address_space(4))) int32_t*)(clen))[c];
+      const int64_t off = w.off;
+      w.off += len;
+      ++w.nc;
+      const int a = max(LO, gs), e = min(HI, gs + len);
+      if (a < e) {
+        const int t = (a - gs) / kTileKeys;
+        w.row = off + static_cast<int64_t>(t) * kTileKeys;
+        w.coord = gs + t * kTileKeys;
+        w.left = (e - gs + kTileKeys - 1) / kTileKeys - t;
+        w.rows_left = len - t * kTileKeys;
+        w.self = 0;
+        break;
+      }
     }
   }
+  out.row0 = w.row;
+  out.nrows = min(kTileKeys, w.rows_left);
+  out.coord0 = w.coord;
+  out.self = w.self;
+  w.row += kTileKeys;
+  w.coord += kTileKeys;
+  w.rows_left -= kTileKeys;
+  --w.left;
+  return true;
 }
 
 // One 64-key tile (K rows, then V rows of one kv head) is copied straight from HBM
@@ -129,10 +134,17 @@ struct TileDma {
     const int64_t first = (t.row0 * hkv + g) * D;  // element offset of the tile's row 0
     const uint32_t lb = lds + static_cast<uint32_t>(w * NI * 1024);
     if (KEEP && t.nrows == kTileKeys) {
+      if constexpr (NI == 4 || NI == 2) {  // a wave's copies all come from K, or all from V
+        static_assert(HALF % (NI * 64) == 0, "a wave's copies stay inside K or inside V");
+        const uint16_t* src = (w * NI * 64 >= HALF ? V : K) + first;
+        if constexpr (NI == 4) dma16_s4(src, voff[0], voff[KEEP ? 1 : 0], voff[KEEP ? 2 : 0], voff[KEEP ? 3 : 0], lb);
+        else dma16_s2(src, voff[0], voff[KEEP ? 1 : 0], lb);
+      } else {
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const bool isv = (w * NI + j) * 64 >= HALF;  // uniform per instruction
-        dma16_s((isv ? V : K) + first, voff[j], lb + 1024 * j);
+        for (int j = 0; j < NI; ++j) {
+          const bool isv = (w * NI + j) * 64 >= HALF;  // uniform per instruction
+          dma16_s((isv ? V : K) + first, voff[KEEP ? j : 0], lb + 1024 * j);
+        }
       }
     } else {
       const uint32_t last = static_cast<uint32_t>(t.nrows - 1);

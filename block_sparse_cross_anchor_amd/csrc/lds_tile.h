@@ -157,6 +157,51 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32
       : "memory");
 }
 
+// Two or four 16-byte copies from one uniform base, to LDS slices lds_base +
+// 1024 j, in one block: m0 is saved and restored once.  An s_nop follows each m0
+// write ahead of the copy that reads it.
+__device__ __forceinline__ void dma16_s2(const void* sbase, uint32_t o0, uint32_t o1, uint32_t lds_base) {
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(lds_base), b1 = b0 + 1024;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o0), "v"(o1), "s"(uniform_ptr(sbase)), "s"(b0), "s"(b1)
+      : "memory");
+}
+
+__device__ __forceinline__ void dma16_s4(const void* sbase, uint32_t o0, uint32_t o1, uint32_t o2, uint32_t o3,
+                                         uint32_t lds_base) {
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(lds_base);
+  const uint32_t b1 = b0 + 1024, b2 = b0 + 2048, b3 = b0 + 3072;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %5\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\t"
+      "s_mov_b32 m0, %9\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o0), "v"(o1), "v"(o2), "v"(o3), "s"(uniform_ptr(sbase)), "s"(b0), "s"(b1), "s"(b2), "s"(b3)
+      : "memory");
+}
+
 __device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
   uint32_t saved;
