@@ -323,8 +323,10 @@ struct StepGeo {
     hcs = (grp + kStepRows - 1) / kStepRows;
     n_steps = (n_q + ts - 1) / ts * hcs;
   }
-  __device__ int tok0(int st) const { return (st / hcs) * ts; }
-  __device__ int h0(int st) const { return (st % hcs) * kStepRows; }
+  // with hcs = 1 (groups of up to 32 heads) a step is ts whole tokens; with hcs > 1,
+  // ts = 1 and a token takes hcs steps: no division in the common case
+  __device__ int tok0(int st) const { return hcs == 1 ? st * ts : st / hcs; }
+  __device__ int h0(int st) const { return hcs == 1 ? 0 : (st % hcs) * kStepRows; }
   __device__ int ntok(int st, int n_q) const { return min(ts, n_q - tok0(st)); }
   // valid rows of a step (a prefix of its 32 rows)
   __device__ int rows(int st, int n_q, int grp) const {
