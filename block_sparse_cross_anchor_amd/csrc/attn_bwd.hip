@@ -298,9 +298,11 @@ constexpr int kStepRows = 32;
 constexpr int kListCap = 2 * 64 * kKvWaves;  // step indices held in LDS at once
 
 // Stream-K list units: a tile with hits occupies kSetupUnits + hits consecutive units
-// of the per-head list (the first ones stand for its setup and write-back, so that a
-// share that starts many short tiles gets fewer steps); a tile without hits, none.
-constexpr int kSetupUnits = 7;
+// of the per-head list (the first ones stand for its setup, step list and write-back,
+// so that a share that starts many short tiles gets fewer steps); a tile without
+// hits, none.  Measured, a segment's fixed work takes about as long as 7 to 9 steps,
+// and the kernel time is flat for weights 9 to 13.
+constexpr int kSetupUnits = 10;
 
 struct DkdvSched {
   int32_t n_ctx_tiles, n_tiles;
