@@ -90,7 +90,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
   constexpr int ROWS = 32 * kDqWaves;
-  using Dma = TileDma<D, kDqWaves, false>;
+  using Dma = TileDma<D, kDqWaves, true>;
   __shared__ __attribute__((aligned(256))) uint16_t bufs[3][Dma::ELEMS];
 
   const int tid = threadIdx.x;
