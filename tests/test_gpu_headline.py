@@ -1,0 +1,90 @@
+"""The benchmark's own step, checked against the oracle on sampled outputs.
+
+One pass of the hot path on the 8192-query x 65536-token workload (Hq 32, Hkv 8,
+d 128, bf16) in exactly the launch configuration the benchmark times: chunk costs,
+the LPT plan onto 8 bins, each bin's gather and forward, the 8-way combine, the
+delta pre-pass, the dQ phase of every bin (accumulated) and the load-balanced dK/dV
+phase of every bin.  Sampled outputs are compared with the oracle, which evaluates
+each of them from the inputs alone:
+  * merged O and lse of sampled blocks (all of their allowed keys),
+  * dQ and the own-block dK, dV of sampled blocks, from the merged O and lse,
+  * dK, dV of 64-key windows of three bins' local buffers, mapped back to their
+    global positions through the plan.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+import oracle
+from helpers import assert_lse_close, host64, rel_frob, sub_blocks, token_rows
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+class _Untimed:
+    def run(self, name, work, fn, launches=1):
+        return fn()
+
+
+def test_benchmark_step_sampled_against_oracle():
+    P = bench.build_problem(torch, 3)
+    bins, load, cost, bin_pairs = bench.step(torch, P, _Untimed())
+    torch.cuda.synchronize()
+    w, meta, inp = P["w"], P["meta"], P["inp"]
+    n_q, hq, d = w.n_q, w.hq, w.d
+    scale = P["scale"]
+    gs_all, gl_all = np.array([0], np.int32), np.array([w.n_ctx], np.int32)
+    q64, k64, v64, do64 = inp.q.f64, inp.k.f64, inp.v.f64, inp.dout.f64
+    ks64, vs64 = inp.k_self.f64, inp.v_self.f64
+    o64 = host64(P["o"].view(n_q, hq, d))
+    lse64 = host64(P["lse"].view(n_q, hq))
+
+    rng = np.random.default_rng(7)
+    starts = np.flatnonzero(np.diff(meta.sample_start) != 0) + 1  # first block of each sample
+    blocks = np.unique(np.concatenate([[0, meta.n_blk - 1], starts[:3], starts[:3] - 1,
+                                       rng.integers(0, meta.n_blk, 4)]))
+    sub = sub_blocks(meta, blocks)
+    rows = token_rows(blocks)
+
+    # merged forward
+    ro, rl = oracle.sparse_xattn_fwd(q64[rows], k64, v64, sub.anchor, sub.sample_start,
+                                     gs_all, gl_all, scale, ks64[rows], vs64[rows])
+    assert np.abs(o64[rows] - ro).max() <= 2e-2
+    assert rel_frob(o64[rows], ro) <= 1e-2
+    assert_lse_close(lse64[rows], rl, 1e-3)
+
+    # dQ and own-block dK, dV of the sampled blocks
+    r = oracle.sparse_xattn_bwd(q64[rows], k64, v64, o64[rows], do64[rows], lse64[rows],
+                                sub.anchor, sub.sample_start, gs_all, gl_all, scale,
+                                ks64[rows], vs64[rows])
+    assert rel_frob(host64(P["dq"])[rows], r[0]) <= 3e-2
+    assert rel_frob(host64(P["dks"])[rows], r[3]) <= 3e-2
+    assert rel_frob(host64(P["dvs"])[rows], r[4]) <= 3e-2
+
+    # dK, dV of local key windows: local row offset + c * chunk_size <-> global chunk start
+    checked = 0
+    for b in (0, 3, 7):
+        gsb = P["plan_gs"][b].cpu().numpy()
+        glb = P["plan_gl"][b].cpu().numpy()
+        offs = np.concatenate([[0], np.cumsum(glb)])
+        for c in rng.choice(len(gsb), 2, replace=False):
+            off = int(rng.integers(0, int(glb[c]) - 64 + 1))
+            g0 = int(gsb[c]) + off
+            l0 = int(offs[c]) + off
+            g1, l1 = np.array([g0], np.int32), np.array([64], np.int32)
+            rr = oracle.sparse_xattn_bwd(q64, k64[g0:g0 + 64], v64[g0:g0 + 64], o64, do64, lse64,
+                                         meta.anchor, meta.sample_start, g1, l1, scale)
+            got_k = host64(P["dk_loc"][b][l0:l0 + 64])
+            got_v = host64(P["dv_loc"][b][l0:l0 + 64])
+            if np.abs(rr[1]).max() == 0:  # no query reads these keys: exact zeros
+                assert not got_k.any() and not got_v.any()
+                continue
+            assert rel_frob(got_k, rr[1]) <= 3e-2, (b, c, off)
+            assert rel_frob(got_v, rr[2]) <= 3e-2, (b, c, off)
+            checked += 1
+    assert checked >= 3
