@@ -139,8 +139,12 @@ def build_problem(torch, seed):
     P["delta"] = torch.empty((2, n_q, hq), dtype=f32, device="cuda")
     P["dq"] = torch.empty((n_q, hq, d), dtype=f32, device="cuda")
     P["cost"] = torch.empty((w.n_chunk,), dtype=torch.int64, device="cuda")
-    P["plan_gs"] = torch.empty((nb, per_bin), dtype=torch.int32, device="cuda")
-    P["plan_gl"] = torch.empty((nb, per_bin), dtype=torch.int32, device="cuda")
+    # the plan's host side in allocated pinned memory: one D2H of the costs and one
+    # H2D of the packed plan per step, neither through a staging copy
+    P["cost_h"] = torch.empty((w.n_chunk,), dtype=torch.int64, pin_memory=True)
+    P["plan_h"] = torch.empty((2, nb, per_bin), dtype=torch.int32, pin_memory=True)
+    P["plan"] = torch.empty((2, nb, per_bin), dtype=torch.int32, device="cuda")
+    P["plan_gs"], P["plan_gl"] = P["plan"][0], P["plan"][1]
     P["per_bin"], P["n_loc"] = per_bin, n_loc
     P["scale"] = 1.0 / math.sqrt(d)
     return P
@@ -155,12 +159,17 @@ def step(torch, P, T):
     scale = P["scale"]
     T.run("chunk_cost", 8 * w.n_anchor + 8 * w.n_chunk,
           lambda: sxattn.chunk_cost(P["anchor"], P["start"], w.n_ctx, w.chunk_size, out=P["cost"]))
-    cost = P["cost"].cpu()                                  # device -> host, synchronises
+    P["cost_h"].copy_(P["cost"])                            # device -> host, synchronises
+    cost = P["cost_h"]
     bins, load = sxattn.lpt_assign(cost, nb)                # host planner
     bins_np = bins.numpy()
     order = np.argsort(bins_np, kind="stable").reshape(nb, per_bin)   # chunks of each bin
-    P["plan_gs"].copy_(torch.from_numpy(P["chunk_gs"][order]))
-    P["plan_gl"].copy_(torch.from_numpy(P["chunk_gl"][order]))
+    plan_h = P["plan_h"].numpy()
+    plan_h[0] = P["chunk_gs"][order]
+    plan_h[1] = P["chunk_gl"][order]
+    # the host buffer is next written after the next step's cost copy, which waits
+    # for this copy
+    P["plan"].copy_(P["plan_h"], non_blocking=True)
     cost_np = cost.numpy()
     bin_pairs = [int(cost_np[order[b]].sum()) for b in range(nb)]
     self_pairs = 16 * w.n_q
