@@ -65,6 +65,15 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     args[9], args[19] = 0.1, sxattn.SXA_BF16
     args[3], args[4] = sxattn.SXA_F32, 0
     assert lib.sparse_xattn_fwd(*args) == sxattn.SXA_EUNSUPPORTED
+    # size limits: more than 4096 kv heads, 2^29 or more query rows
+    args[3], args[19] = sxattn.SXA_BF16, sxattn.SXA_BF16
+    args[6], args[7] = 8192, 8192
+    assert lib.sparse_xattn_fwd(*args) == sxattn.SXA_EUNSUPPORTED
+    assert b"hkv" in lib.sxa_last_error()
+    args[6], args[7], args[4] = 4, 2, 1 << 23  # 2^23 blocks x 16 x 4 heads = 2^29 rows
+    assert lib.sparse_xattn_fwd(*args) == sxattn.SXA_EUNSUPPORTED
+    assert b"2^29" in lib.sxa_last_error()
+    args[4] = 1
     # combine: unsupported d
     assert lib.lse_combine(null, 1, null, 1, 10, 96, null, 1, null, null) == sxattn.SXA_EUNSUPPORTED
     # a good call clears the message
