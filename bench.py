@@ -22,6 +22,11 @@ phase (one pair per step around its 8 launches): recording an event costs GPU ti
 so events around every launch would slow the step they measure.  The per-phase
 breakdown comes from the warm-up steps, which carry events around every phase.  The
 CPU oracle is timed on a bounded sample of blocks of the same workload.
+
+`--balance WORKLOAD` runs the per-bin balance study instead (one JSON line): every
+bin's share of the context alone on the GPU under three plans (LPT on the pair cost,
+LPT on a tile-granular cost, contiguous chunks), and how well per-chunk costs and a
+dispatch model predict the per-bin kernel times.
 """
 
 from __future__ import annotations
@@ -277,6 +282,208 @@ def cpu_baseline(P, seconds):
                       f"{pairs} allowed pairs per head"}
 
 
+def tile_costs(meta, n_ctx, chunk_size, hq, hkv):
+    """Per-chunk work at the kernels' own granularity, in (query token, key) slots, for
+    the balance study.  The pair cost counts only allowed pairs; these count whole
+    tiles, edge tiles included:
+      fwd_tiles   64-key tiles (aligned to the chunk start) that a forward / dQ row
+                  group visits: the tiles meeting [min sample start, max anchor) over
+                  the group's blocks, times the group's tokens;
+      blk_tiles   64-key tiles meeting each block's own interval, times 16;
+      dkdv_tiles  256-key tiles meeting each block's interval, times 16.
+    Also returns the forward's 64-key tile count per (row group, chunk)."""
+    lo = meta.sample_start.astype(np.int64)
+    hi = meta.anchor.astype(np.int64)
+    cs = np.arange(0, n_ctx, chunk_size, dtype=np.int64)
+    ce = np.minimum(cs + chunk_size, n_ctx)
+
+    def tiles(lo_g, hi_g, tk):
+        a = np.maximum(lo_g[:, None], cs[None, :])
+        e = np.minimum(hi_g[:, None], ce[None, :])
+        n = -(-(e - cs[None, :]) // tk) - (a - cs[None, :]) // tk
+        return np.where(a < e, n, 0)
+
+    tok = 256 // (hq // hkv)          # tokens of a 256-row group
+    bpg = max(tok // 16, 1)           # blocks per row group
+    ng = -(-meta.n_blk // bpg)
+    pad = ng * bpg - meta.n_blk
+    lo_r = np.concatenate([lo, np.full(pad, lo[-1])]).reshape(ng, bpg).min(1)
+    hi_r = np.concatenate([hi, np.full(pad, hi[-1])]).reshape(ng, bpg).max(1)
+    group_tiles = tiles(lo_r, hi_r, 64)
+    return {"fwd_tiles": (tok * 64 * group_tiles).sum(0),
+            "blk_tiles": (16 * 64 * tiles(lo, hi, 64)).sum(0),
+            "dkdv_tiles": (16 * 256 * tiles(lo, hi, 256)).sum(0)}, group_tiles
+
+
+def dispatch_makespan(job_tiles, n_cu, overhead):
+    """Finish time, in tile times, of jobs (one per forward / dQ workgroup) handed out
+    in the kernels' dispatch order (most tiles first) to the first free compute unit,
+    one at a time per unit, each costing its tiles plus a fixed overhead."""
+    import heapq
+
+    free = [0.0] * n_cu
+    for t in sorted(job_tiles, reverse=True):
+        heapq.heappush(free, heapq.heappop(free) + t + overhead)
+    return max(free)
+
+
+def _fit(x, y):
+    """Least-squares line y = a + b x: (R^2, largest |residual| / y)."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    A = np.stack([np.ones_like(x), x], 1)
+    coef = np.linalg.lstsq(A, y, rcond=None)[0]
+    res = y - A @ coef
+    ss = float(((y - y.mean()) ** 2).sum())
+    return (1.0 - float((res ** 2).sum()) / ss if ss > 0 else 1.0), float(np.abs(res / y).max())
+
+
+def balance_study(torch, workload, seed, reps):
+    """Each bin's share of the context run alone on the GPU, under the LPT plan on the
+    pair cost, the LPT plan on the forward's tile cost and the contiguous plan (bin b
+    = chunks [b n/P, (b+1) n/P)).  Prints one JSON line with the per-bin kernel times
+    of every plan, the max-bin time of each, and how well each per-chunk cost
+    predicts the per-bin kernel times."""
+    from block_sparse_cross_anchor_amd import synth, sxattn
+
+    w = synth.WORKLOADS[workload]
+    if not w.n_bin:
+        raise SystemExit(f"workload {workload} has no bins")
+    meta = synth.meta_for(w, seed)
+    log(f"drawing the {w.n_ctx}-token context ...")
+    inp = synth.draw_inputs(seed, meta, w.hq, w.hkv, w.d, "bf16", w.std(),
+                            np.array([0], np.int32), np.array([w.n_ctx], np.int32),
+                            with_dout=True)
+
+    def dev(t):
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(
+            torch.bfloat16).cuda()
+
+    q, k, v, ks, vs, do = (dev(t) for t in (inp.q, inp.k, inp.v, inp.k_self, inp.v_self, inp.dout))
+    del inp
+    anchor = torch.as_tensor(meta.anchor).cuda()
+    start = torch.as_tensor(meta.sample_start).cuda()
+    n_q, hq, hkv, d, nb = w.n_q, w.hq, w.hkv, w.d, w.n_bin
+    per_bin = w.n_chunk // nb
+    n_loc = per_bin * w.chunk_size
+    scale = 1.0 / math.sqrt(d)
+    gs_all, gl_all = synth.contiguous_chunks(w.n_ctx, w.chunk_size)
+    cost = sxattn.chunk_cost(anchor, start, w.n_ctx, w.chunk_size).cpu().numpy()
+    tc, group_tiles = tile_costs(meta, w.n_ctx, w.chunk_size, hq, hkv)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    plans = {"lpt_pairs": sxattn.lpt_assign(cost, nb)[0].numpy(),
+             "lpt_fwd_tiles": sxattn.lpt_assign(tc["fwd_tiles"], nb)[0].numpy(),
+             "contiguous": np.arange(w.n_chunk, dtype=np.int32) // per_bin}
+    bf, f32 = torch.bfloat16, torch.float32
+    k_loc = torch.empty((n_loc, hkv, d), dtype=bf, device="cuda")
+    v_loc = torch.empty_like(k_loc)
+    dk = torch.empty((n_loc, hkv, d), dtype=f32, device="cuda")
+    dv = torch.empty_like(dk)
+    o_p = torch.empty((n_q, hq, d), dtype=bf, device="cuda")
+    lse_p = torch.empty((n_q, hq), dtype=f32, device="cuda")
+    dq = torch.empty((n_q, hq, d), dtype=f32, device="cuda")
+    delta = torch.empty((2, n_q, hq), dtype=f32, device="cuda")
+
+    def share(bins_np, b):
+        chunks = np.flatnonzero(bins_np == b)
+        gsb = torch.as_tensor(gs_all[chunks]).cuda()
+        glb = torch.as_tensor(gl_all[chunks]).cuda()
+        sxattn.context_gather(k, gsb, glb, n_loc, out=k_loc)
+        sxattn.context_gather(v, gsb, glb, n_loc, out=v_loc)
+        return sxattn.Meta(anchor, start, gsb, glb, n_loc=n_loc), chunks
+
+    # combined O and lse of the whole pass (own-block term included), which every
+    # backward share reads
+    log("combined forward ...")
+    o_parts = torch.empty((nb, n_q, hq, d), dtype=bf, device="cuda")
+    lse_parts = torch.empty((nb, n_q, hq), dtype=f32, device="cuda")
+    for b in range(nb):
+        m, _ = share(plans["lpt_pairs"], b)
+        sxattn.sparse_xattn_fwd(q, k_loc, v_loc, m, scale, ks if b == 0 else None,
+                                vs if b == 0 else None, out=o_parts[b], lse=lse_parts[b])
+    o, lse = sxattn.lse_combine(o_parts.view(nb, n_q * hq, d), lse_parts.view(nb, n_q * hq))
+    del o_parts, lse_parts
+    o, lse = o.view(n_q, hq, d), lse.view(n_q, hq)
+    m0, _ = share(plans["lpt_pairs"], 0)
+    sxattn.sparse_xattn_bwd(q, k_loc, v_loc, m0, scale, o, do, lse, dq, delta_ws=delta,
+                            dk=dk, dv=dv, flags=sxattn.BWD_DELTA)
+    phases = {
+        "fwd": lambda m: sxattn.sparse_xattn_fwd(q, k_loc, v_loc, m, scale, out=o_p, lse=lse_p),
+        "dq": lambda m: sxattn.sparse_xattn_bwd(q, k_loc, v_loc, m, scale, o, do, lse, dq,
+                                                delta_ws=delta, dk=dk, dv=dv,
+                                                flags=sxattn.BWD_DQ | sxattn.BWD_DQ_OVERWRITE),
+        "dkdv": lambda m: sxattn.sparse_xattn_bwd(q, k_loc, v_loc, m, scale, o, do, lse, dq,
+                                                  delta_ws=delta, dk=dk, dv=dv,
+                                                  flags=sxattn.BWD_DKDV),
+    }
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(len(plans) * nb * len(phases))]
+    preds = {"pairs": cost, **tc}
+    out = {"study": "balance", "workload": workload, "seed": seed, "bins": nb,
+           "chunks": w.n_chunk, "reps": reps, "plans": {}}
+    rows = []   # (plan, bin, phase ms..., predictor loads..., forward jobs' tiles)
+    i = 0
+    for name, bins_np in plans.items():
+        log(f"plan {name} ...")
+        per = {ph: [] for ph in phases}
+        loads = {pn: [] for pn in preds}
+        for b in range(nb):
+            m, chunks = share(bins_np, b)
+            for pn, pv in preds.items():
+                loads[pn].append(int(pv[chunks].sum()))
+            for ph, fn in phases.items():
+                fn(m)   # warm
+                e0, e1 = ev[i]
+                i += 1
+                e0.record()
+                for _ in range(reps):
+                    fn(m)
+                e1.record()
+                per[ph].append((e0, e1))
+        torch.cuda.synchronize()
+        ms = {ph: [e0.elapsed_time(e1) / reps for e0, e1 in per[ph]] for ph in phases}
+        tot = [sum(ms[ph][b] for ph in phases) for b in range(nb)]
+        for b in range(nb):
+            jobs = np.repeat(group_tiles[:, bins_np == b].sum(1), hkv)
+            rows.append((name, b, {ph: ms[ph][b] for ph in phases}, tot[b],
+                         {pn: loads[pn][b] for pn in preds}, jobs))
+        out["plans"][name] = {
+            "max_bin_ms": round(max(tot), 4), "mean_bin_ms": round(float(np.mean(tot)), 4),
+            "time_imbalance": round(max(tot) / float(np.mean(tot)) - 1, 4),
+            "phase_max_ms": {ph: round(max(ms[ph]), 4) for ph in phases},
+            "load_imbalance": {pn: round(max(loads[pn]) / float(np.mean(loads[pn])) - 1, 4)
+                               for pn in preds},
+            "per_bin_ms": [round(t, 4) for t in tot],
+            "per_bin_phase_ms": {ph: [round(t, 4) for t in ms[ph]] for ph in phases},
+        }
+    out["contiguous_over_lpt_pairs"] = round(out["plans"]["contiguous"]["max_bin_ms"]
+                                             / out["plans"]["lpt_pairs"]["max_bin_ms"], 3)
+    fits = {}
+    for ph in list(phases) + ["total"]:
+        y = [r[3] if ph == "total" else r[2][ph] for r in rows]
+        fits[ph] = {}
+        for pn in preds:
+            r2, worst = _fit([r[4][pn] for r in rows], y)
+            fits[ph][pn] = {"r2": round(r2, 4), "max_rel_residual": round(worst, 4)}
+    # the dispatch model for the two row-group kernels, its overhead fitted on a grid
+    for ph in ("fwd", "dq"):
+        y = [r[2][ph] for r in rows]
+        best = None
+        for ov in range(0, 17):
+            x = [dispatch_makespan(r[5], n_cu, ov) for r in rows]
+            r2, worst = _fit(x, y)
+            if best is None or r2 > best[0]:
+                best = (r2, worst, ov)
+        fits[ph]["dispatch_model"] = {"r2": round(best[0], 4), "max_rel_residual": round(best[1], 4),
+                                      "overhead_tiles": best[2]}
+    out["fits"] = fits
+    out["fits_note"] = ("line fitted to the per-bin kernel time over every bin of every "
+                        "plan, against each per-chunk cost summed over the bin's chunks; "
+                        "dispatch_model: against the makespan of the forward's row-group jobs "
+                        f"on {n_cu} compute units, each costing its tiles plus a fitted overhead")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +492,10 @@ def main():
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--balance", metavar="WORKLOAD",
+                    help="instead of the benchmark, the per-bin balance study of a workload "
+                         "with bins (fwd_bf16_8kq_64k or cp64_share_8kq_512k)")
+    ap.add_argument("--reps", type=int, default=5, help="launches per timed share (--balance)")
     args = ap.parse_args()
     if args.warmup < 1 or args.steps < 1:
         ap.error("--steps and --warmup must be at least 1")
@@ -302,6 +513,9 @@ def main():
 
     sxattn.load_library()
     torch.cuda.set_device(0)
+    if args.balance:
+        balance_study(torch, args.balance, args.seed, max(args.reps, 1))
+        return
     log("building the synthetic workload ...")
     P = build_problem(torch, args.seed)
     w = P["w"]

@@ -156,8 +156,12 @@ def meta_for(w: Workload, seed: int) -> Meta:
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit pattern, round to nearest even (inputs are finite)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    # in 32-bit words: a finite value's bits plus at most 0x8000 stay below 2^32
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    odd = (u >> 16) & 1
+    u += 0x7FFF
+    u += odd
+    u >>= 16
     return u.astype(np.uint16)
 
 
@@ -201,19 +205,29 @@ def draw_normal(seed: int, tag: int, shape, std: float, dtype: str, sub: int = 0
 
 def draw_context(seed: int, tag: int, rows: np.ndarray, h: int, d: int, std: float,
                  dtype: str) -> Tensor:
-    """Context tensor values at the given global rows (granule-wise streams)."""
+    """Context tensor values at the given global rows (granule-wise streams).  Each
+    granule's values are drawn, scaled and rounded on their own, so the output is
+    built piecewise without whole-tensor temporaries."""
     rows = np.asarray(rows, dtype=np.int64)
-    out = np.empty((rows.shape[0], h, d), dtype=np.float32)
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(dtype)
+    out = np.empty((rows.shape[0], h, d), dtype=np.uint16 if dtype == "bf16" else np.float32)
     if rows.size:
         gran = rows // GRANULE
-        for g in np.unique(gran):
+        order = np.argsort(gran, kind="stable")   # rows grouped by granule
+        ug, first = np.unique(gran[order], return_index=True)
+        ends = np.append(first[1:], order.size)
+        for g, a, e in zip(ug, first, ends):
             rng = _rng(seed, tag, int(g))
             block = rng.standard_normal(size=(GRANULE, h, d), dtype=np.float32)
-            sel = gran == g
-            out[sel] = block[rows[sel] - g * GRANULE]
-    if std != 1.0:
-        out *= np.float32(std)
-    return _finish(out, dtype)
+            if std != 1.0:
+                block *= np.float32(std)
+            sel = order[a:e]
+            if sel[-1] - sel[0] == e - a - 1 and np.all(np.diff(sel) == 1):   # a run of rows
+                sel = slice(int(sel[0]), int(sel[-1]) + 1)
+            vals = block[rows[sel] - g * GRANULE]
+            out[sel] = f32_to_bf16_bits(vals) if dtype == "bf16" else vals
+    return Tensor(out, dtype)
 
 
 def chunk_rows(chunk_gstart, chunk_len) -> np.ndarray:
