@@ -8,7 +8,8 @@ tokens and planned onto 8 virtual devices ("bins"):
   1. chunk_cost   realised cost of each chunk (GPU, int64), copied to the host
   2. lpt_assign   longest-processing-time-first plan with equal chunk counts (host)
   3. per bin: context_gather of its chunks of K and V into its local buffer, then
-     sparse_xattn_fwd (the own-block term on bin 0): partial O, lse
+     sparse_xattn_fwd (the own-block term on bin 0): partial O, lse; the bins
+     alternate between two streams, so their gathers and forwards overlap
   4. lse_combine  of the 8 partials
   5. sparse_xattn_bwd: delta pre-pass, then the dQ phase of every bin (accumulated)
      and the dK/dV phase of every bin
@@ -76,7 +77,8 @@ class Timers:
                      for _ in range(n)]
         self.pool.reverse()
 
-    def run(self, name, work, fn, launches=1):
+    def run(self, name, work, fn, launches=1, stream=None):
+        """Run fn, with events on `stream` (default: the current stream) around it."""
         if self.only is None:
             self.calls[name] = self.calls.get(name, 0) + 1
             return fn()
@@ -85,9 +87,9 @@ class Timers:
         if not self.pool:
             raise RuntimeError("Timers: more timed phases than reserved events")
         e0, e1 = self.pool.pop()
-        e0.record()
+        e0.record(stream)
         out = fn()
-        e1.record()
+        e1.record(stream)
         self.pending.append((name, work, launches, e0, e1))
         return out
 
@@ -152,6 +154,16 @@ def build_problem(torch, seed):
     P["plan_gs"], P["plan_gl"] = P["plan"][0], P["plan"][1]
     P["per_bin"], P["n_loc"] = per_bin, n_loc
     P["scale"] = 1.0 / math.sqrt(d)
+    # The bins' gathers and forwards alternate between the current stream and a
+    # second one (default priority), so one bin's forward overlaps the other
+    # stream's gather and the tail of its forward.  Each stream has its own forward
+    # workspace; the two events that fork and join the streams are created here,
+    # outside any timed region.
+    P["side_stream"] = torch.cuda.Stream()
+    P["ev_fork"] = torch.cuda.Event()
+    P["ev_join"] = torch.cuda.Event()
+    fws = int(sxattn.load_library().sparse_xattn_fwd_workspace_bytes(w.n_anchor, hq, hkv))
+    P["fwd_ws"] = [torch.empty((max(fws, 256),), dtype=torch.uint8, device="cuda") for _ in range(2)]
     return P
 
 
@@ -181,20 +193,32 @@ def step(torch, P, T):
     row_bytes = w.hkv * d * 2
     metas = []
     for b in range(nb):
-        gsb, glb = P["plan_gs"][b], P["plan_gl"][b]
-        for src, dst in ((P["k"], P["k_loc"][b]), (P["v"], P["v_loc"][b])):
-            T.run("context_gather", 2 * n_loc * row_bytes,
-                  lambda src=src, dst=dst: sxattn.context_gather(src, gsb, glb, n_loc, out=dst))
         m = sxattn.Meta.__new__(sxattn.Meta)
-        m.anchor, m.sample_start, m.chunk_gstart, m.chunk_len = P["anchor"], P["start"], gsb, glb
+        m.anchor, m.sample_start = P["anchor"], P["start"]
+        m.chunk_gstart, m.chunk_len = P["plan_gs"][b], P["plan_gl"][b]
         m.n_blk, m.n_chunk, m.n_loc = w.n_anchor, per_bin, n_loc
         metas.append(m)
-        pairs = bin_pairs[b] + (self_pairs if b == 0 else 0)
-        T.run("sparse_xattn_fwd", 4.0 * d * hq * pairs,
-              lambda b=b: sxattn.sparse_xattn_fwd(
-                  P["q"], P["k_loc"][b], P["v_loc"][b], metas[b], scale,
-                  P["ks"] if b == 0 else None, P["vs"] if b == 0 else None,
-                  out=P["o_parts"][b], lse=P["lse_parts"][b]))
+    main, side = torch.cuda.current_stream(), P["side_stream"]
+    fwd_pairs = sum(bin_pairs) + self_pairs
+
+    def gathers_and_forwards():
+        # the side stream starts after the plan upload (and after everything the
+        # previous step queued on the current stream, which reads the buffers it
+        # rewrites); the current stream continues once both are done
+        P["ev_fork"].record(main)
+        side.wait_event(P["ev_fork"])
+        for b in range(nb):
+            with torch.cuda.stream(main if b % 2 == 0 else side):
+                for src, dst in ((P["k"], P["k_loc"][b]), (P["v"], P["v_loc"][b])):
+                    sxattn.context_gather(src, P["plan_gs"][b], P["plan_gl"][b], n_loc, out=dst)
+                sxattn.sparse_xattn_fwd(
+                    P["q"], P["k_loc"][b], P["v_loc"][b], metas[b], scale,
+                    P["ks"] if b == 0 else None, P["vs"] if b == 0 else None,
+                    out=P["o_parts"][b], lse=P["lse_parts"][b], workspace=P["fwd_ws"][b % 2])
+        P["ev_join"].record(side)
+        main.wait_event(P["ev_join"])
+
+    T.run("gather_fwd", 4.0 * d * hq * fwd_pairs, gathers_and_forwards, launches=nb)
     rows = w.n_q * hq
     T.run("lse_combine", nb * rows * (d * 2 + 4) + rows * (d * 2 + 4),
           lambda: sxattn.lse_combine(P["o_parts"].view(nb, rows, d), P["lse_parts"].view(nb, rows),
@@ -534,8 +558,10 @@ def main():
     else:
         per_kernel = {}
     # the dominant phase: the most time per step in the breakdown (the backward's
-    # dK/dV phase when there is no breakdown)
-    dom = max(per_kernel, key=lambda n: per_kernel[n]["ms"]) if per_kernel else "bwd_dkdv"
+    # dK/dV phase when there is no breakdown), among the phases whose launches run
+    # one after another on one stream (so that a launch's events time that kernel)
+    single = {n: k for n, k in per_kernel.items() if n != "gather_fwd"}
+    dom = max(single, key=lambda n: single[n]["ms"]) if single else "bwd_dkdv"
     T.reserve(per_step[dom] * args.steps)
     T.only = dom
     log(f"timing {args.steps} steps ...")
@@ -566,7 +592,7 @@ def main():
     kernels = {}   # from the warm-up steps with events around every phase
     n_bd = max(args.warmup - 1, 1)
     for n, k in per_kernel.items():
-        mf = n in ("sparse_xattn_fwd", "bwd_dq", "bwd_dkdv")
+        mf = n in ("gather_fwd", "bwd_dq", "bwd_dkdv")
         rate = k["work"] / (k["ms"] * 1e-3) / (1e12 if mf else 1e9)
         kernels[n] = {"ms_per_step": round(k["ms"] / n_bd, 4),
                       ("TFLOP/s" if mf else "GB/s"): round(rate, 1)}
@@ -583,7 +609,9 @@ def main():
                    "lpt_imbalance": round(float(load.max() / load.mean() - 1), 5)},
         "roofline": roofline,
         "kernels": kernels,
-        "kernels_note": f"per-phase times from {n_bd} warm-up steps with events around every phase",
+        "kernels_note": f"per-phase times from {n_bd} warm-up steps with events around every phase; "
+                        "gather_fwd is the bins' context gathers and forwards on two streams, its "
+                        "rate the forward's FLOP over that span",
     }
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")
