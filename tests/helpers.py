@@ -51,3 +51,33 @@ def sub_blocks(meta, blocks):
 
 def token_rows(blocks, block=16):
     return np.concatenate([np.arange(b * block, (b + 1) * block) for b in blocks])
+
+
+def readers(meta, g0, g1):
+    """Blocks whose context interval [sample_start, anchor) meets the keys [g0, g1)."""
+    return np.flatnonzero((meta.sample_start < g1) & (meta.anchor > g0))
+
+
+def pick_windows(meta, chunk_gstart, chunk_len, rng, n, cap, width=64, tries=400):
+    """Up to n key windows of `width` local rows inside single chunks, each read by 1 to
+    `cap` blocks: (local row, global position, reader blocks)."""
+    offs = np.concatenate([[0], np.cumsum(chunk_len)])
+    out = []
+    for _ in range(tries):
+        c = int(rng.integers(0, len(chunk_gstart)))
+        if chunk_len[c] < width:
+            continue
+        off = int(rng.integers(0, int(chunk_len[c]) - width + 1))
+        g0 = int(chunk_gstart[c]) + off
+        r = readers(meta, g0, g0 + width)
+        if 1 <= r.size <= cap and all(g0 != w[1] for w in out):
+            out.append((int(offs[c]) + off, g0, r))
+            if len(out) == n:
+                break
+    return out
+
+
+def head_rows(blocks, hq, block=16):
+    """Rows of the flattened [n_q * hq] layout that belong to the given blocks."""
+    t = token_rows(blocks, block)
+    return (t[:, None] * hq + np.arange(hq)[None, :]).ravel()
