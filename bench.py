@@ -24,6 +24,9 @@ so events around every launch would slow the step they measure.  The per-phase
 breakdown comes from the warm-up steps, which carry events around every phase.  The
 CPU oracle is timed on a bounded sample of blocks of the same workload.
 
+`--dense KEYS` times the forward, dQ and dK/dV phases of one dense call instead
+(8192 queries that may all read KEYS keys; one JSON line).
+
 `--balance WORKLOAD` runs the per-bin balance study instead (one JSON line): every
 bin's share of the context alone on the GPU under three plans (LPT on the pair cost,
 LPT on a tile-granular cost, contiguous chunks), and how well per-chunk costs and a
@@ -508,6 +511,57 @@ def balance_study(torch, workload, seed, reps):
     print(json.dumps(out), flush=True)
 
 
+def dense_study(torch, n_keys, seed, reps):
+    """Forward, dQ and dK/dV phases of one dense call: 8192 queries (512 blocks) that
+    may all read every one of n_keys context keys (one chunk, no own-block term),
+    Hq 32, Hkv 8, d 128, bf16.  Prints one JSON line with each phase's time per call
+    (HIP events around `reps` back-to-back calls) and its rate at 4d, 6d and 8d FLOP
+    per pair."""
+    from block_sparse_cross_anchor_amd import synth, sxattn
+
+    n_blk, hq, hkv, d = 512, 32, 8, 128
+    n_q = 16 * n_blk
+    meta = synth.Meta(np.array([n_keys], np.int64), np.array([0], np.int64),
+                      np.full(n_blk, n_keys, np.int32), np.zeros(n_blk, np.int32), n_keys)
+    gs, gl = np.array([0], np.int32), np.array([n_keys], np.int32)
+    inp = synth.draw_inputs(seed, meta, hq, hkv, d, "bf16", 1.0 / math.sqrt(d), gs, gl,
+                            self_block=False, with_dout=True)
+
+    def dev(t):
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(
+            torch.bfloat16).cuda()
+
+    q, k, v, do = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.dout)
+    dm = sxattn.Meta(meta.anchor, meta.sample_start, gs, gl)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = sxattn.sparse_xattn_fwd(q, k, v, dm, scale)
+    dq = torch.zeros((n_q, hq, d), dtype=torch.float32, device="cuda")
+    delta = torch.empty((2, n_q, hq), dtype=torch.float32, device="cuda")
+    dk = torch.empty((n_keys, hkv, d), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    bwd = lambda flags: sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o, do, lse, dq, delta_ws=delta,
+                                                dk=dk, dv=dv, flags=flags)
+    bwd(sxattn.BWD_DELTA)
+    phases = {"fwd": (4, lambda: sxattn.sparse_xattn_fwd(q, k, v, dm, scale, out=o, lse=lse)),
+              "dq": (6, lambda: bwd(sxattn.BWD_DQ | sxattn.BWD_DQ_OVERWRITE)),
+              "dkdv": (8, lambda: bwd(sxattn.BWD_DKDV))}
+    out = {"study": "dense", "n_q": n_q, "n_keys": n_keys, "hq": hq, "hkv": hkv, "head_dim": d,
+           "reps": reps}
+    pairs = n_q * n_keys
+    for name, (per_pair, fn) in phases.items():
+        fn()   # warm
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4),
+                     "TFLOP/s": round(per_pair * d * hq * pairs / (ms * 1e-3) / 1e12, 1)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -519,7 +573,11 @@ def main():
     ap.add_argument("--balance", metavar="WORKLOAD",
                     help="instead of the benchmark, the per-bin balance study of a workload "
                          "with bins (fwd_bf16_8kq_64k or cp64_share_8kq_512k)")
-    ap.add_argument("--reps", type=int, default=5, help="launches per timed share (--balance)")
+    ap.add_argument("--reps", type=int, default=5,
+                    help="launches per timed share (--balance) or phase (--dense)")
+    ap.add_argument("--dense", type=int, metavar="KEYS",
+                    help="instead of the benchmark, the dense 8192-query x KEYS call of each "
+                         "attention phase")
     args = ap.parse_args()
     if args.warmup < 1 or args.steps < 1:
         ap.error("--steps and --warmup must be at least 1")
@@ -539,6 +597,9 @@ def main():
     torch.cuda.set_device(0)
     if args.balance:
         balance_study(torch, args.balance, args.seed, max(args.reps, 1))
+        return
+    if args.dense:
+        dense_study(torch, args.dense, args.seed, max(args.reps, 1))
         return
     log("building the synthetic workload ...")
     P = build_problem(torch, args.seed)
