@@ -24,6 +24,9 @@ so events around every launch would slow the step they measure.  The per-phase
 breakdown comes from the warm-up steps, which carry events around every phase.  The
 CPU oracle is timed on a bounded sample of blocks of the same workload.
 
+`--combine P` times the P-way combine of the 8192-query view instead (every partial
+live, and the empty pattern of the 524288-token workload on P bins; one JSON line).
+
 `--dense KEYS` times the forward, dQ and dK/dV phases of one dense call instead
 (8192 queries that may all read KEYS keys; one JSON line).
 
@@ -562,6 +565,70 @@ def dense_study(torch, n_keys, seed, reps):
     print(json.dumps(out), flush=True)
 
 
+def combine_study(torch, n_parts, seed, reps):
+    """lse_combine of n_parts bf16 partials for every row of the 8192-query view
+    (8192 x 32 heads, d 128), the merge one device performs at context-parallel size
+    n_parts.  Two cases: every partial live (lse ~ U(0, 10), O ~ N(0, 0.1^2)), and
+    the empty pattern of the 524288-token workload planned onto n_parts bins (a
+    partial is empty, lse = -inf, where the block's interval meets none of that bin's
+    chunks; the kernel never reads such a partial's O).  Eight seeded partial sets are
+    drawn and repeated across the n_parts slots.  Prints one JSON line with each
+    case's time per call and its rate in algorithmic bytes (O rows of live partials,
+    every lse, the output)."""
+    from block_sparse_cross_anchor_amd import synth, sxattn
+
+    w = synth.WORKLOADS["cp64_share_8kq_512k"]
+    n_q, hq, d = w.n_q, w.hq, w.d
+    rows = n_q * hq
+    o_parts = torch.empty((n_parts, rows, d), dtype=torch.bfloat16, device="cuda")
+    n_draw = min(8, n_parts)
+    for i in range(n_draw):
+        o_i, _ = synth.draw_partials(seed + 100 * i, 1, rows, d, "bf16")
+        src = torch.from_numpy(o_i.bits.view(np.int16)).view(torch.bfloat16).cuda()[0]
+        for p in range(i, n_parts, n_draw):
+            o_parts[p].copy_(src)
+        del o_i, src
+    rng = np.random.default_rng(seed)
+    lse_dense = torch.as_tensor(rng.uniform(0.0, 10.0, size=(n_parts, rows)).astype(np.float32)).cuda()
+    # the real empty pattern: LPT plan of the 524288-token workload onto n_parts bins
+    meta = synth.meta_for(w, 5)
+    cost = sxattn.chunk_cost(torch.as_tensor(meta.anchor).cuda(),
+                             torch.as_tensor(meta.sample_start).cuda(), w.n_ctx,
+                             w.chunk_size).cpu()
+    bins = sxattn.lpt_assign(cost, n_parts)[0].numpy()
+    gs_all, gl_all = synth.contiguous_chunks(w.n_ctx, w.chunk_size)
+    lo = meta.sample_start.astype(np.int64)[:, None]
+    hi = meta.anchor.astype(np.int64)[:, None]
+    cs = gs_all.astype(np.int64)[None, :]
+    meets = np.maximum(lo, cs) < np.minimum(hi, cs + gl_all[None, :])       # [n_blk, n_chunk]
+    live_blk = np.stack([meets[:, bins == p].any(1) for p in range(n_parts)])  # [P, n_blk]
+    live_blk[0] = True   # the own-block term lives on bin 0: its partial is never empty
+    live = np.repeat(live_blk, 16 * hq, axis=1)                             # [P, rows]
+    lse_empty = lse_dense.clone()
+    lse_empty[torch.as_tensor(~live).cuda()] = float("-inf")
+    out_o = torch.empty((rows, d), dtype=torch.bfloat16, device="cuda")
+    out_l = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    result = {"study": "combine", "parts": n_parts, "rows": rows, "head_dim": d, "dtype": "bf16",
+              "reps": reps, "peak_GB/s": PEAK_HBM_GBS}
+    for name, lse, live_rows in (("all_live", lse_dense, n_parts * rows),
+                                 ("empty_pattern", lse_empty, int(live.sum()))):
+        fn = lambda: sxattn.lse_combine(o_parts, lse, out=out_o, lse_out=out_l)
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = live_rows * d * 2 + n_parts * rows * 4 + rows * (d * 2 + 4)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        result[name] = {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+                        "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                        "live_fraction": round(live_rows / (n_parts * rows), 4)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -575,6 +642,8 @@ def main():
                          "with bins (fwd_bf16_8kq_64k or cp64_share_8kq_512k)")
     ap.add_argument("--reps", type=int, default=5,
                     help="launches per timed share (--balance) or phase (--dense)")
+    ap.add_argument("--combine", type=int, metavar="P",
+                    help="instead of the benchmark, the P-way lse_combine of the 8192-query view")
     ap.add_argument("--dense", type=int, metavar="KEYS",
                     help="instead of the benchmark, the dense 8192-query x KEYS call of each "
                          "attention phase")
@@ -600,6 +669,9 @@ def main():
         return
     if args.dense:
         dense_study(torch, args.dense, args.seed, max(args.reps, 1))
+        return
+    if args.combine:
+        combine_study(torch, args.combine, args.seed, max(args.reps, 1))
         return
     log("building the synthetic workload ...")
     P = build_problem(torch, args.seed)

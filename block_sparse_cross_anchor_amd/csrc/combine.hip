@@ -7,11 +7,13 @@
 //   m = max_p lse_p,  lse = m + ln sum_p exp(lse_p - m),  O = sum_p exp(lse_p - lse) O_p.
 // Partials with lse_p = -inf are skipped without reading their O_p.
 //
-// The kernel is HBM-bound: it streams every O_p row once.  16 lanes own one row
+// The kernel is HBM-bound: it streams every live O_p row once, with non-temporal
+// loads (each row is read exactly once; 64-way: 5.3 -> 5.7 TB/s measured).  16 lanes own one row
 // (each lane D/16 consecutive elements, 16 B for bf16 at D = 128), so each partial
 // row is one fully coalesced 256 B (bf16) segment.  The statistics pass reads the
-// P lse values of the row (strided by `rows`), the streaming pass issues the O_p
-// loads of 8 partials before consuming them to keep enough bytes in flight.
+// P lse values of the row (strided by `rows`); the streaming pass issues the loads
+// of 8 partials before their sums.  With more than 8 partials it walks only the
+// live ones (a bit mask per row), so empty partials take no slot of a batch.
 #include "device_common.h"
 #include "internal.h"
 
@@ -21,14 +23,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerBlock = kThreads / kLanesPerRow;
-constexpr int kBatch = 8;
+constexpr int kMaxBatch = 8;
 
 template <typename T, int EPL>
 struct Vec;
 template <>
 struct Vec<uint16_t, 8> {
   u32x4 raw;
-  __device__ __forceinline__ void load(const uint16_t* p) { raw = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void load(const uint16_t* p) { raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
   __device__ __forceinline__ float get(int i) const {
     uint32_t w = raw[i >> 1];
     return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -37,7 +39,7 @@ struct Vec<uint16_t, 8> {
 template <>
 struct Vec<uint16_t, 4> {
   u32x2 raw;
-  __device__ __forceinline__ void load(const uint16_t* p) { raw = *reinterpret_cast<const u32x2*>(p); }
+  __device__ __forceinline__ void load(const uint16_t* p) { raw = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)); }
   __device__ __forceinline__ float get(int i) const {
     uint32_t w = raw[i >> 1];
     return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -47,8 +49,8 @@ template <>
 struct Vec<uint16_t, 16> {
   u32x4 raw[2];
   __device__ __forceinline__ void load(const uint16_t* p) {
-    raw[0] = reinterpret_cast<const u32x4*>(p)[0];
-    raw[1] = reinterpret_cast<const u32x4*>(p)[1];
+    raw[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    raw[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
   }
   __device__ __forceinline__ float get(int i) const {
     uint32_t w = raw[i >> 3][(i >> 1) & 3];
@@ -60,7 +62,7 @@ struct Vec<float, EPL> {
   f32x4 raw[EPL / 4];
   __device__ __forceinline__ void load(const float* p) {
 #pragma unroll
-    for (int i = 0; i < EPL / 4; ++i) raw[i] = reinterpret_cast<const f32x4*>(p)[i];
+    for (int i = 0; i < EPL / 4; ++i) raw[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + i);
   }
   __device__ __forceinline__ float get(int i) const { return raw[i >> 2][i & 3]; }
 };
@@ -111,7 +113,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const TIn* __restrict
                                                            TOut* __restrict__ o_out,
                                                            float* __restrict__ lse_out) {
   constexpr int EPL = D / kLanesPerRow;
+  constexpr int kBatch = kMaxBatch;  // loads issued before their sums
   const int lane = threadIdx.x % kLanesPerRow;
+  const int grp_shift = (threadIdx.x % 64) & ~(kLanesPerRow - 1);  // this row's lanes in the wave
   const int64_t row_raw = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + threadIdx.x / kLanesPerRow;
   const bool live_row = row_raw < rows;
   const int64_t row = live_row ? row_raw : rows - 1;  // keep every lane in the shuffles
@@ -131,23 +135,60 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const TIn* __restrict
 #pragma unroll
     for (int off = kLanesPerRow / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kLanesPerRow);
     lse = m + __logf(s);
-    const TIn* base = o_parts + row * D + lane * EPL;
-    const int64_t pstride = rows * D;
-    for (int p0 = 0; p0 < n_parts; p0 += kBatch) {
-      float w[kBatch];
+  }
+  const TIn* base = o_parts + row * D + lane * EPL;
+  const int64_t pstride = rows * D;
+  if (n_parts <= kBatch) {
+    // one batch: every partial's load issued before the sums (empty ones skipped)
+    if (lse != -INFINITY) {
       Vec<TIn, EPL> x[kBatch];
+      float w[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const int p = p0 + j;
-        const float l = p < n_parts ? lse_parts[p * rows + row] : -INFINITY;
+        const float l = j < n_parts ? lse_parts[j * rows + row] : -INFINITY;
         w[j] = l == -INFINITY ? 0.f : __expf(l - lse);
-        if (w[j] != 0.f) x[j].load(base + p * pstride);
+        if (w[j] != 0.f) x[j].load(base + j * pstride);
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         if (w[j] != 0.f) {
 #pragma unroll
           for (int i = 0; i < EPL; ++i) acc[i] = fmaf(w[j], x[j].get(i), acc[i]);
+        }
+      }
+    }
+  } else {
+    // 64 partials at a time: the row's live partials (finite lse) as a bit mask,
+    // then their O rows in ascending order, kBatch loads issued before their sums.
+    // Empty partials are never read and take no slot of a batch.  The 16 lanes of a
+    // row hold the same mask, so the loops below are uniform within the row.
+    for (int c0 = 0; c0 < n_parts; c0 += 64) {
+      uint64_t mask = 0;
+#pragma unroll
+      for (int k = 0; k < 64 / kLanesPerRow; ++k) {
+        const int p = c0 + kLanesPerRow * k + lane;
+        const bool live = lse != -INFINITY && p < n_parts && lse_parts[p * rows + row] != -INFINITY;
+        mask |= ((__ballot(live) >> grp_shift) & ((uint64_t{1} << kLanesPerRow) - 1)) << (kLanesPerRow * k);
+      }
+      while (mask != 0) {
+        Vec<TIn, EPL> x[kBatch];
+        float w[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          w[j] = 0.f;
+          if (mask != 0) {
+            const int p = c0 + __builtin_ctzll(mask);
+            mask &= mask - 1;
+            w[j] = __expf(lse_parts[p * rows + row] - lse);
+            x[j].load(base + p * pstride);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (w[j] != 0.f) {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) acc[i] = fmaf(w[j], x[j].get(i), acc[i]);
+          }
         }
       }
     }
