@@ -166,7 +166,16 @@ def build_problem(torch, seed):
     # workspace; the two events that fork and join the streams are created here,
     # outside any timed region.
     P["side_stream"] = torch.cuda.Stream()
+    # each bin's call metadata: views of the device plan, which every step rewrites
+    P["metas"] = []
+    for b in range(nb):
+        m = sxattn.Meta.__new__(sxattn.Meta)
+        m.anchor, m.sample_start = P["anchor"], P["start"]
+        m.chunk_gstart, m.chunk_len = P["plan_gs"][b], P["plan_gl"][b]
+        m.n_blk, m.n_chunk, m.n_loc = w.n_anchor, per_bin, n_loc
+        P["metas"].append(m)
     P["ev_fork"] = torch.cuda.Event()
+    P["ev_cost"] = torch.cuda.Event()
     P["ev_join"] = torch.cuda.Event()
     fws = int(sxattn.load_library().sparse_xattn_fwd_workspace_bytes(w.n_anchor, hq, hkv))
     P["fwd_ws"] = [torch.empty((max(fws, 256),), dtype=torch.uint8, device="cuda") for _ in range(2)]
@@ -182,7 +191,12 @@ def step(torch, P, T):
     scale = P["scale"]
     T.run("chunk_cost", 8 * w.n_anchor + 8 * w.n_chunk,
           lambda: sxattn.chunk_cost(P["anchor"], P["start"], w.n_ctx, w.chunk_size, out=P["cost"]))
-    P["cost_h"].copy_(P["cost"])                            # device -> host, synchronises
+    # device -> host; the host polls the copy's event instead of blocking in the copy,
+    # so it resumes as soon as the costs have landed
+    P["cost_h"].copy_(P["cost"], non_blocking=True)
+    P["ev_cost"].record()
+    while not P["ev_cost"].query():
+        pass
     cost = P["cost_h"]
     bins, load = sxattn.lpt_assign(cost, nb)                # host planner
     bins_np = bins.numpy()
@@ -194,18 +208,10 @@ def step(torch, P, T):
     # for this copy
     P["plan"].copy_(P["plan_h"], non_blocking=True)
     cost_np = cost.numpy()
-    bin_pairs = [int(cost_np[order[b]].sum()) for b in range(nb)]
     self_pairs = 16 * w.n_q
-    row_bytes = w.hkv * d * 2
-    metas = []
-    for b in range(nb):
-        m = sxattn.Meta.__new__(sxattn.Meta)
-        m.anchor, m.sample_start = P["anchor"], P["start"]
-        m.chunk_gstart, m.chunk_len = P["plan_gs"][b], P["plan_gl"][b]
-        m.n_blk, m.n_chunk, m.n_loc = w.n_anchor, per_bin, n_loc
-        metas.append(m)
+    metas = P["metas"]
     main, side = torch.cuda.current_stream(), P["side_stream"]
-    fwd_pairs = sum(bin_pairs) + self_pairs
+    fwd_pairs = int(cost_np.sum()) + self_pairs
 
     def gathers_and_forwards():
         # the side stream starts after the plan upload (and after everything the
@@ -225,6 +231,7 @@ def step(torch, P, T):
         main.wait_event(P["ev_join"])
 
     T.run("gather_fwd", 4.0 * d * hq * fwd_pairs, gathers_and_forwards, launches=nb)
+    bin_pairs = [int(cost_np[order[b]].sum()) for b in range(nb)]   # after the launches
     rows = w.n_q * hq
     T.run("lse_combine", nb * rows * (d * 2 + 4) + rows * (d * 2 + 4),
           lambda: sxattn.lse_combine(P["o_parts"].view(nb, rows, d), P["lse_parts"].view(nb, rows),
