@@ -176,8 +176,30 @@ def build_problem(torch, seed):
         P["metas"].append(m)
     P["ev_fork"] = torch.cuda.Event()
     P["ev_cost"] = torch.cuda.Event()
+    P["ev_fork_dq"] = torch.cuda.Event()
+    P["ev_join_dq"] = torch.cuda.Event()
     P["ev_join"] = torch.cuda.Event()
-    fws = int(sxattn.load_library().sparse_xattn_fwd_workspace_bytes(w.n_anchor, hq, hkv))
+    # The dQ phase runs as two halves of the blocks, one per stream: blocks are
+    # independent and the halves write disjoint dQ rows.  Each half has its own call
+    # metadata, delta buffer (a call's delta planes are laid out for its own rows)
+    # and workspace.
+    lib = sxattn.load_library()
+    half = w.n_anchor // 2
+    P["dq_halves"] = []
+    for b0, b1 in ((0, half), (half, w.n_anchor)):
+        hm = []
+        for b in range(nb):
+            m = sxattn.Meta.__new__(sxattn.Meta)
+            m.anchor, m.sample_start = P["anchor"][b0:b1], P["start"][b0:b1]
+            m.chunk_gstart, m.chunk_len = P["plan_gs"][b], P["plan_gl"][b]
+            m.n_blk, m.n_chunk, m.n_loc = b1 - b0, per_bin, n_loc
+            hm.append(m)
+        bws = int(lib.sparse_xattn_bwd_workspace_bytes(b1 - b0, n_loc, hq, hkv, d))
+        P["dq_halves"].append({
+            "tok": slice(16 * b0, 16 * b1), "metas": hm,
+            "delta": torch.empty((2, 16 * (b1 - b0), hq), dtype=f32, device="cuda"),
+            "ws": torch.empty((max(bws, 256),), dtype=torch.uint8, device="cuda")})
+    fws = int(lib.sparse_xattn_fwd_workspace_bytes(w.n_anchor, hq, hkv))
     P["fwd_ws"] = [torch.empty((max(fws, 256),), dtype=torch.uint8, device="cuda") for _ in range(2)]
     return P
 
@@ -238,12 +260,39 @@ def step(torch, P, T):
                                      out=P["o"], lse_out=P["lse"]))
     o = P["o"].view(w.n_q, hq, d)
     lse = P["lse"].view(w.n_q, hq)
-    T.run("delta", rows * (2 * d * 2 + 4),
-          lambda: sxattn.sparse_xattn_bwd(P["q"], P["k_loc"][0], P["v_loc"][0], metas[0], scale, o,
-                                          P["do"], lse, P["dq"], delta_ws=P["delta"],
-                                          dk=P["dk_loc"][0], dv=P["dv_loc"][0],
-                                          flags=sxattn.BWD_DELTA))
+    halves = P["dq_halves"]
+
+    def half_args(hf, b):
+        t = hf["tok"]
+        return (P["q"][t], P["k_loc"][b], P["v_loc"][b], hf["metas"][b], scale, o[t], P["do"][t],
+                lse[t], P["dq"][t])
+
+    def deltas():   # the whole rows (for dK/dV), then each dQ half's own
+        sxattn.sparse_xattn_bwd(P["q"], P["k_loc"][0], P["v_loc"][0], metas[0], scale, o, P["do"],
+                                lse, P["dq"], delta_ws=P["delta"], dk=P["dk_loc"][0],
+                                dv=P["dv_loc"][0], flags=sxattn.BWD_DELTA)
+        for hf in halves:
+            sxattn.sparse_xattn_bwd(*half_args(hf, 0), delta_ws=hf["delta"], dk=P["dk_loc"][0],
+                                    dv=P["dv_loc"][0], flags=sxattn.BWD_DELTA, workspace=hf["ws"])
+
+    T.run("delta", 2 * rows * (2 * d * 2 + 4), deltas, launches=3)
     all_pairs = sum(bin_pairs) + self_pairs
+
+    def dq_halves():
+        P["ev_fork_dq"].record(main)
+        side.wait_event(P["ev_fork_dq"])
+        for i, hf in enumerate(halves):
+            t = hf["tok"]
+            with torch.cuda.stream(main if i == 0 else side):
+                for b in range(nb):
+                    sxattn.sparse_xattn_bwd(
+                        *half_args(hf, b), P["ks"][t] if b == 0 else None,
+                        P["vs"][t] if b == 0 else None, delta_ws=hf["delta"], dk=P["dk_loc"][b],
+                        dv=P["dv_loc"][b], dk_self=P["dks"][t], dv_self=P["dvs"][t],
+                        flags=sxattn.BWD_DQ | (sxattn.BWD_DQ_OVERWRITE if b == 0 else 0),
+                        workspace=hf["ws"])
+        P["ev_join_dq"].record(side)
+        main.wait_event(P["ev_join_dq"])
 
     def bwd(b, flags):
         self_kv = (P["ks"], P["vs"]) if b == 0 else (None, None)
@@ -252,10 +301,9 @@ def step(torch, P, T):
             self_kv[0], self_kv[1], delta_ws=P["delta"], dk=P["dk_loc"][b], dv=P["dv_loc"][b],
             dk_self=P["dks"], dv_self=P["dvs"], flags=flags)
 
-    # each phase as one group of nb launches (bin 0 overwrites dQ, the others add)
-    T.run("bwd_dq", 6.0 * d * hq * all_pairs,
-          lambda: [bwd(b, sxattn.BWD_DQ | (sxattn.BWD_DQ_OVERWRITE if b == 0 else 0)) for b in range(nb)],
-          launches=nb)
+    # dQ: both halves' bins on two streams (bin 0 overwrites a half's rows, the others
+    # add); dK/dV: one group of nb launches on this stream
+    T.run("bwd_dq", 6.0 * d * hq * all_pairs, dq_halves, launches=2 * nb)
     T.run("bwd_dkdv", 8.0 * d * hq * all_pairs,
           lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)], launches=nb)
     return bins_np, load.numpy(), cost_np, bin_pairs
@@ -700,7 +748,7 @@ def main():
     # the dominant phase: the most time per step in the breakdown (the backward's
     # dK/dV phase when there is no breakdown), among the phases whose launches run
     # one after another on one stream (so that a launch's events time that kernel)
-    single = {n: k for n, k in per_kernel.items() if n != "gather_fwd"}
+    single = {n: k for n, k in per_kernel.items() if n not in ("gather_fwd", "bwd_dq")}
     dom = max(single, key=lambda n: single[n]["ms"]) if single else "bwd_dkdv"
     T.reserve(per_step[dom] * args.steps)
     T.only = dom
@@ -751,7 +799,8 @@ def main():
         "kernels": kernels,
         "kernels_note": f"per-phase times from {n_bd} warm-up steps with events around every phase; "
                         "gather_fwd is the bins' context gathers and forwards on two streams, its "
-                        "rate the forward's FLOP over that span",
+                        "rate the forward's FLOP over that span; bwd_dq runs two halves of the "
+                        "query blocks on two streams",
     }
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")

@@ -2,11 +2,12 @@
 
 One pass of the hot path on the 8192-query x 65536-token workload (Hq 32, Hkv 8,
 d 128, bf16) in exactly the launch configuration the benchmark times: chunk costs,
-the LPT plan onto 8 bins, each bin's gather and forward (the gathers on a stream of
-their own, the forwards alternating between two streams), the 8-way combine, the
-delta pre-pass, the dQ phase of every bin (accumulated) and the load-balanced dK/dV
-phase of every bin.  Sampled outputs are compared with the oracle, which evaluates
-each of them from the inputs alone (its backward consumes its own merged forward):
+the LPT plan onto 8 bins, each bin's gather and forward (the bins alternating
+between two streams), the 8-way combine, the delta pre-pass, the dQ phase of every
+bin (accumulated; two halves of the query blocks on two streams) and the
+load-balanced dK/dV phase of every bin.  Sampled outputs are compared with the
+oracle, which evaluates each of them from the inputs alone (its backward consumes
+its own merged forward):
   * merged O and lse of sampled blocks (all of their allowed keys),
   * dQ and the own-block dK, dV of sampled blocks,
   * dK, dV of 64-key windows of three bins' local buffers (windows read by at most
