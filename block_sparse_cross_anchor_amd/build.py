@@ -81,5 +81,27 @@ def build(verbose: bool = True, out: str = OUT, defines=()) -> str:
     return out
 
 
+DRIVER_SRC = os.path.join(ROOT, "tests", "c_abi", "sxattn_c_driver.cpp")
+DRIVER_OUT = os.path.join(ROOT, "tests", "c_abi", "sxattn_c_driver")
+
+
+def build_c_driver(verbose: bool = True) -> str:
+    """Compile the host program that drives the library through its C ABI alone
+    (used by the GPU tests); it finds libsxattn.so next to this file at run time."""
+    if not os.path.exists(DRIVER_SRC):
+        return ""
+    tmp = DRIVER_OUT + ".tmp"
+    cmd = [_hipcc(), "-O2", "-std=c++17", "-Wall", "-I", INCLUDE, DRIVER_SRC, "-o", tmp,
+           "-L", HERE, "-lsxattn", "-Wl,-rpath,$ORIGIN/../../block_sparse_cross_anchor_amd"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"driver build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, DRIVER_OUT)
+    if verbose:
+        print(f"built {DRIVER_OUT}")
+    return DRIVER_OUT
+
+
 if __name__ == "__main__":
     build()
+    build_c_driver()
