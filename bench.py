@@ -111,7 +111,7 @@ class Timers:
         return agg
 
 
-def build_problem(torch, seed):
+def build_problem(torch, seed, fwd_split=False):
     from block_sparse_cross_anchor_amd import synth, sxattn
 
     w = synth.WORKLOADS[WORKLOAD]
@@ -199,7 +199,8 @@ def build_problem(torch, seed):
             "tok": slice(16 * b0, 16 * b1), "metas": hm,
             "delta": torch.empty((2, 16 * (b1 - b0), hq), dtype=f32, device="cuda"),
             "ws": torch.empty((max(bws, 256),), dtype=torch.uint8, device="cuda")})
-    fws = int(lib.sparse_xattn_fwd_workspace_bytes(w.n_anchor, hq, hkv))
+    fws = int(lib.sparse_xattn_fwd_split_workspace_bytes(w.n_anchor, hq, hkv, d) if fwd_split
+              else lib.sparse_xattn_fwd_workspace_bytes(w.n_anchor, hq, hkv))
     P["fwd_ws"] = [torch.empty((max(fws, 256),), dtype=torch.uint8, device="cuda") for _ in range(2)]
     return P
 
@@ -412,6 +413,17 @@ def dispatch_makespan(job_tiles, n_cu, overhead):
     return max(free)
 
 
+def split_jobs(job_tiles, cap, merge):
+    """Row-group jobs as a split-KV forward would run them: a job of t > cap tiles
+    becomes ceil(t / cap) pieces of equal share, each also paying `merge` tiles for
+    writing its partial output and its part of the merge."""
+    out = []
+    for t in job_tiles:
+        s = max(1, -(-int(t) // cap))
+        out += [t / s + (merge if s > 1 else 0)] * s
+    return out
+
+
 def _fit(x, y):
     """Least-squares line y = a + b x: (R^2, largest |residual| / y)."""
     x = np.asarray(x, np.float64)
@@ -494,6 +506,8 @@ def balance_study(torch, workload, seed, reps):
                             dk=dk, dv=dv, flags=sxattn.BWD_DELTA)
     phases = {
         "fwd": lambda m: sxattn.sparse_xattn_fwd(q, k_loc, v_loc, m, scale, out=o_p, lse=lse_p),
+        "fwd_split": lambda m: sxattn.sparse_xattn_fwd(q, k_loc, v_loc, m, scale, out=o_p, lse=lse_p,
+                                                       workspace="split"),
         "dq": lambda m: sxattn.sparse_xattn_bwd(q, k_loc, v_loc, m, scale, o, do, lse, dq,
                                                 delta_ws=delta, dk=dk, dv=dv,
                                                 flags=sxattn.BWD_DQ | sxattn.BWD_DQ_OVERWRITE),
@@ -527,7 +541,7 @@ def balance_study(torch, workload, seed, reps):
                 per[ph].append((e0, e1))
         torch.cuda.synchronize()
         ms = {ph: [e0.elapsed_time(e1) / reps for e0, e1 in per[ph]] for ph in phases}
-        tot = [sum(ms[ph][b] for ph in phases) for b in range(nb)]
+        tot = [sum(ms[ph][b] for ph in phases if ph != "fwd_split") for b in range(nb)]
         for b in range(nb):
             jobs = np.repeat(group_tiles[:, bins_np == b].sum(1), hkv)
             rows.append((name, b, {ph: ms[ph][b] for ph in phases}, tot[b],
@@ -544,7 +558,7 @@ def balance_study(torch, workload, seed, reps):
     out["contiguous_over_lpt_pairs"] = round(out["plans"]["contiguous"]["max_bin_ms"]
                                              / out["plans"]["lpt_pairs"]["max_bin_ms"], 3)
     fits = {}
-    for ph in list(phases) + ["total"]:
+    for ph in [ph for ph in phases if ph != "fwd_split"] + ["total"]:
         y = [r[3] if ph == "total" else r[2][ph] for r in rows]
         fits[ph] = {}
         for pn in preds:
@@ -562,6 +576,26 @@ def balance_study(torch, workload, seed, reps):
         fits[ph]["dispatch_model"] = {"r2": round(best[0], 4), "max_rel_residual": round(best[1], 4),
                                       "overhead_tiles": best[2]}
     out["fits"] = fits
+    # split-KV inside one call, under the fitted dispatch model: the slowest bin of the
+    # LPT plan with long jobs split, over the same bin unsplit
+    lpt_rows = [r for r in rows if r[0] == "lpt_pairs"]
+    out["split_model"] = {}
+    for ph in ("fwd", "dq"):
+        ov = fits[ph]["dispatch_model"]["overhead_tiles"]
+        base = max(dispatch_makespan(r[5], n_cu, ov) for r in lpt_rows)
+        out["split_model"][ph] = {
+            f"cap_{cap}": round(max(dispatch_makespan(split_jobs(r[5], cap, 1), n_cu, ov)
+                                    for r in lpt_rows) / base, 3)
+            for cap in (8, 16, 32, 64)}
+    out["split_measured"] = {
+        name: {"fwd_max_bin_ms": p["phase_max_ms"]["fwd"],
+               "fwd_split_max_bin_ms": p["phase_max_ms"]["fwd_split"],
+               "ratio": round(p["phase_max_ms"]["fwd_split"] / p["phase_max_ms"]["fwd"], 3)}
+        for name, p in out["plans"].items()}
+    out["split_model_note"] = ("modelled max-bin time of the LPT plan with every row-group "
+                               "job over cap tiles split into equal pieces (each paying the "
+                               "fitted overhead plus one tile for its partial and merge), relative to "
+                               "no split; below 1 would favour splitting")
     out["fits_note"] = ("line fitted to the per-bin kernel time over every bin of every "
                         "plan, against each per-chunk cost summed over the bin's chunks; "
                         "dispatch_model: against the makespan of the forward's row-group jobs "
@@ -692,6 +726,8 @@ def main():
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fwd-split", action="store_true",
+                    help="run the step's forwards on the split schedule (split workspaces)")
     ap.add_argument("--balance", metavar="WORKLOAD",
                     help="instead of the benchmark, the per-bin balance study of a workload "
                          "with bins (fwd_bf16_8kq_64k or cp64_share_8kq_512k)")
@@ -729,7 +765,7 @@ def main():
         combine_study(torch, args.combine, args.seed, max(args.reps, 1))
         return
     log("building the synthetic workload ...")
-    P = build_problem(torch, args.seed)
+    P = build_problem(torch, args.seed, fwd_split=args.fwd_split)
     w = P["w"]
     T = Timers(torch)
     log(f"warmup {args.warmup} steps ...")
@@ -792,6 +828,7 @@ def main():
         "config": {"workload": WORKLOAD, "n_q": w.n_q, "n_ctx": w.n_ctx, "hq": w.hq,
                    "hkv": w.hkv, "head_dim": w.d, "block": 16, "chunks": w.n_chunk,
                    "chunk_size": w.chunk_size, "bins": w.n_bin, "seed": args.seed,
+                   "fwd_schedule": "split" if args.fwd_split else "ranked",
                    "allowed_pairs_per_head": pairs, "pct_of_bf16_peak": round(
                        100 * value / PEAK_BF16_TFLOPS, 2),
                    "lpt_imbalance": round(float(load.max() / load.mean() - 1), 5)},

@@ -116,6 +116,16 @@ int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_d
   if (workspace_bytes < 0) return fail(SXA_EINVAL, "workspace_bytes must be >= 0");
   const int64_t need = sparse_xattn_fwd_workspace_bytes(n_blk, hq, hkv);
   if (workspace != nullptr && need > 0 && workspace_bytes >= need) a.rg_order = static_cast<int32_t*>(workspace);
+  a.fwd_split = nullptr;
+  a.n_cu = 0;
+  if (workspace != nullptr && in_dtype == SXA_BF16) {
+    const int32_t n_cu = sxa::n_compute_units();
+    const int64_t split = sxa::fwd_split_bytes(n_blk, hq, hkv, d, n_cu);
+    if (split > 0 && workspace_bytes >= split) {
+      a.fwd_split = workspace;
+      a.n_cu = n_cu;
+    }
+  }
   if (n_blk == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(in_dtype == SXA_BF16 ? sxa::launch_fwd_bf16(a, s) : sxa::launch_fwd_f32(a, s),
@@ -181,6 +191,11 @@ int64_t sparse_xattn_fwd_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv)
   a.hkv = hkv;
   const int64_t groups = sxa::row_groups(a, sxa::kRowsPerGroup);
   return 4 * (groups < sxa::kMaxOrderedGroups ? groups : sxa::kMaxOrderedGroups);
+}
+
+int64_t sparse_xattn_fwd_split_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv, int32_t d) {
+  if (n_blk < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || (d != 64 && d != 128)) return 0;
+  return sxa::fwd_split_bytes(n_blk, hq, hkv, d, sxa::n_compute_units());
 }
 
 int64_t sparse_xattn_bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hq, int32_t hkv, int32_t d) {

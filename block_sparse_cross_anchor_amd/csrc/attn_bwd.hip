@@ -901,17 +901,6 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, DkdvSched
   }
 }
 
-int n_compute_units() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev < 64) cached[dev] = n;
-  return n;
-}
-
 struct WsLayout {
   int64_t n_tiles, n_shares, prefix_off, tinfo_off, coord_off, order_off, slots_off, bytes;
 };

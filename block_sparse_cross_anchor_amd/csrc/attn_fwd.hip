@@ -64,6 +64,11 @@ struct FwdParams {
   void* o;
   float* lse;
   const int32_t* rg_order;  // row group of workgroup blockIdx / hkv (nullptr: identity)
+  // split forward (jobs != nullptr): job blockIdx / hkv = {row group, first tile, end
+  // tile, slot}; a job with a slot writes its partial O and lse there
+  const int4* jobs;
+  float* part_o;
+  float* part_lse;
   int32_t n_blk, hq, hkv, n_chunk;
   float scale_log2;  // scale * log2(e)
 };
@@ -84,7 +89,16 @@ fwd_bf16_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
   const int g = blockIdx.x % p.hkv;
-  const int wg = p.rg_order ? p.rg_order[blockIdx.x / p.hkv] : static_cast<int>(blockIdx.x / p.hkv);
+  int wg, t_skip = 0, t_left = 0x7fffffff;
+  if (p.jobs) {
+    const int4 jb = p.jobs[blockIdx.x / p.hkv];
+    if (jb.x < 0) return;  // more job slots than jobs
+    wg = jb.x;
+    t_skip = jb.y;
+    t_left = jb.z - jb.y;
+  } else {
+    wg = p.rg_order ? p.rg_order[blockIdx.x / p.hkv] : static_cast<int>(blockIdx.x / p.hkv);
+  }
   const int grp = p.hq / p.hkv;
   const int64_t R = static_cast<int64_t>(p.n_blk) * kBlock * grp;
   const int64_t wg_row0 = static_cast<int64_t>(wg) * ROWS;
@@ -99,6 +113,14 @@ fwd_bf16_kernel(FwdParams p) {
 
   Walk w;
   w.start(p.k_self != nullptr, b_first, b_last);
+  // a piece of a split row group: skip to its first tile, stop after its last
+  Tile skipped;
+  for (int i = 0; i < t_skip; ++i) walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, skipped);
+  auto next_tile = [&](Tile& t) {
+    if (t_left == 0) return false;
+    --t_left;
+    return walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, t);
+  };
 
   float m[NT], l[NT];
   f32x16 oacc[DT][NT];
@@ -113,11 +135,20 @@ fwd_bf16_kernel(FwdParams p) {
   }
 
   Tile cur;
-  const bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
+  const bool have = next_tile(cur);
   if (!have) {  // no allowed key in this call: O = 0, lse = -inf
+    const int slot = p.jobs ? p.jobs[blockIdx.x / p.hkv].w : -1;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int64_t r = wg_row0 + 32 * NT * wave + 32 * nt + l32;
+      const int lr = 32 * NT * wave + 32 * nt + l32;
+      const int64_t r = wg_row0 + lr;
+      if (slot >= 0) {
+        const int64_t pr = (static_cast<int64_t>(slot) * p.hkv + g) * ROWS + lr;
+        if (h2 == 0) p.part_lse[pr] = -INFINITY;
+        for (int d0 = h2 * (D / 2); d0 < (h2 + 1) * (D / 2); d0 += 4)
+          *reinterpret_cast<f32x4*>(p.part_o + pr * D + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+        continue;
+      }
       if (r >= R) continue;
       const int64_t tok = r / grp;
       const int64_t orow = tok * p.hq + static_cast<int64_t>(g) * grp + static_cast<int>(r % grp);
@@ -175,7 +206,7 @@ fwd_bf16_kernel(FwdParams p) {
   dma.issue(cur, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[0]));
   bool have1 = false;
   if constexpr (NSTAGE == 3) {
-    have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
+    have1 = next_tile(n1);
     if (have1) dma.issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[1]));
   }
   int cb = 0;
@@ -185,12 +216,12 @@ fwd_bf16_kernel(FwdParams p) {
       if (have1) wait_vmcnt<Dma::NI>();  // this wave's DMA of `cur` done (n1 may be in flight)
       else wait_vmcnt<0>();
       barrier_nofence();                 // ... and every wave's; all reads of the third buffer are done
-      have2 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);  // false once exhausted
+      have2 = next_tile(n2);  // false once exhausted
       if (have2) dma.issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[cb == 0 ? 2 : cb - 1]));
     } else {
       wait_vmcnt<0>();
       barrier_nofence();  // `cur` landed everywhere; the other buffer is no longer read
-      have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
+      have1 = next_tile(n1);
       if (have1) dma.issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[cb ^ 1]));
     }
       // per-lane constants are redefined opaquely per tile so that derived addresses
@@ -329,7 +360,27 @@ fwd_bf16_kernel(FwdParams p) {
     }
   }
 
-  // ---- epilogue: normalise, write O and lse
+  // ---- epilogue: normalise, write O and lse (a piece: its slot, float32)
+  const int slot = p.jobs ? p.jobs[blockIdx.x / p.hkv].w : -1;
+  if (slot >= 0) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float lt = l[nt] + swap_halves(l[nt]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int64_t pr = (static_cast<int64_t>(slot) * p.hkv + g) * ROWS + 32 * NT * wave + 32 * nt + l32;
+      if (h2 == 0) p.part_lse[pr] = lt > 0.f ? (m[nt] + __log2f(lt)) * kLn2 : -INFINITY;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d0 = 32 * dt + 8 * jj + 4 * h2;
+          *reinterpret_cast<f32x4*>(p.part_o + pr * D + d0) =
+              f32x4{oacc[dt][nt][4 * jj] * inv, oacc[dt][nt][4 * jj + 1] * inv, oacc[dt][nt][4 * jj + 2] * inv,
+                    oacc[dt][nt][4 * jj + 3] * inv};
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float lt = l[nt] + swap_halves(l[nt]);
@@ -353,6 +404,71 @@ fwd_bf16_kernel(FwdParams p) {
           *reinterpret_cast<f32x4*>(O) = f32x4{x0, x1, x2, x3};
         }
       }
+  }
+}
+
+// Merge of a split row group's pieces.  One workgroup per (split group, kv head,
+// run of kMergeRowsPerLane * 256 / (d / 4) rows); d / 4 lanes share a row, each
+// lane takes kMergeRowsPerLane rows in one pass (rows merged in a loop would each
+// pay a round of memory latency; 4 rows per lane measured slower than 1).  Per
+// row: lse = M + ln sum_k exp(lse_k - M) with M the largest piece lse, and
+// O = sum_k exp(lse_k - lse) O_k; a row no piece reaches gets O = 0, lse = -inf.
+// Workgroups of unused split-group entries return at once.
+constexpr int kMergeRowsPerLane = 1;
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdSplit sp, void* o, float* lse, int32_t n_blk, int32_t hq,
+                                                        int32_t hkv) {
+  constexpr int LPR = D / 4;                      // lanes per row, 4 values each
+  constexpr int RPL = kMergeRowsPerLane;
+  constexpr int RPW = 256 / LPR * RPL;            // rows per workgroup
+  constexpr int RUNS = kRowsPerGroup / RPW;       // workgroups per (split group, kv head)
+  const int g = blockIdx.x % hkv;
+  const int run = (blockIdx.x / hkv) % RUNS;
+  const int4 jb = sp.groups[blockIdx.x / hkv / RUNS];
+  if (jb.x < 0) return;
+  const int grp = hq / hkv;
+  const int64_t R = static_cast<int64_t>(n_blk) * kBlock * grp;
+  const int sub = threadIdx.x % LPR;
+  int lr[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) lr[i] = run * RPW + i * (256 / LPR) + threadIdx.x / LPR;  // < kRowsPerGroup
+  auto prow = [&](int k, int i) { return (static_cast<int64_t>(jb.y + k) * hkv + g) * kRowsPerGroup + lr[i]; };
+  float mx[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) mx[i] = -INFINITY;
+  for (int k = 0; k < jb.z; ++k)
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) mx[i] = fmaxf(mx[i], sp.part_lse[prow(k, i)]);
+  f32x4 acc[RPL];
+  float den[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    den[i] = 0.f;
+  }
+  for (int k = 0; k < jb.z; ++k)
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      // exp(-inf) = 0; a row with every piece at -inf keeps den = 0
+      const float wk = mx[i] == -INFINITY ? 0.f : expf(sp.part_lse[prow(k, i)] - mx[i]);
+      den[i] += wk;
+      acc[i] += wk * *reinterpret_cast<const f32x4*>(sp.part_o + prow(k, i) * D + 4 * sub);
+    }
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) {
+    const int64_t r = static_cast<int64_t>(jb.x) * kRowsPerGroup + lr[i];
+    if (r >= R) continue;
+    const f32x4 out = acc[i] * (den[i] > 0.f ? 1.f / den[i] : 0.f);
+    const int64_t orow = (r / grp) * hq + static_cast<int64_t>(g) * grp + static_cast<int>(r % grp);
+    if (sub == 0) lse[orow] = den[i] > 0.f ? mx[i] + logf(den[i]) : -INFINITY;
+    if constexpr (OUT_BF16) {
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow * D + 4 * sub) = u32x2{
+          static_cast<uint32_t>(f32_to_bf16_bits(out[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(out[1])) << 16),
+          static_cast<uint32_t>(f32_to_bf16_bits(out[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(out[3])) << 16)};
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow * D + 4 * sub) = out;
+    }
   }
 }
 
@@ -385,6 +501,9 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   p.o = a.o;
   p.lse = a.lse;
   p.rg_order = a.rg_order;
+  p.jobs = nullptr;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
   p.n_blk = a.n_blk;
   p.hq = a.hq;
   p.hkv = a.hkv;
@@ -394,6 +513,24 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   const int64_t groups = (rows + kRowsPerWG - 1) / kRowsPerWG;
   const int64_t n_wg = groups * a.hkv;
   if (n_wg == 0) return hipSuccess;
+  if (a.fwd_split != nullptr && groups <= kMaxOrderedGroups && kRowsPerWG == kRowsPerGroup) {
+    const FwdSplit sp = fwd_split_layout(a.fwd_split, a);
+    hipError_t e = launch_fwd_split_plan(a, sp, s);
+    if (e != hipSuccess) return e;
+    p.rg_order = nullptr;
+    p.jobs = sp.jobs;
+    p.part_o = sp.part_o;
+    p.part_lse = sp.part_lse;
+    fwd_bf16_kernel<D, kNT, kWaves, kStages, OUT_BF16>
+        <<<dim3(static_cast<unsigned>((groups + sp.max_pieces) * a.hkv)), dim3(64 * kWaves), 0, s>>>(p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int kRuns = kRowsPerGroup / (256 / (D / 4) * kMergeRowsPerLane);
+    fwd_merge_kernel<D, OUT_BF16>
+        <<<dim3(static_cast<unsigned>(sp.max_pieces / 2 * a.hkv * kRuns)), dim3(256), 0, s>>>(sp, a.o, a.lse, a.n_blk,
+                                                                                           a.hq, a.hkv);
+    return hipGetLastError();
+  }
   if (p.rg_order != nullptr) {
     if (groups > kMaxOrderedGroups || kRowsPerWG != kRowsPerGroup) {
       p.rg_order = nullptr;

@@ -22,7 +22,8 @@ SXA_OK, SXA_EINVAL, SXA_EUNSUPPORTED, SXA_EHIP = 0, -1, -2, -3
 BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_DQ_OVERWRITE = 1, 2, 4, 8
 BLOCK = 16
 
-EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_fwd_workspace_bytes", "sparse_xattn_bwd",
+EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_fwd_workspace_bytes",
+           "sparse_xattn_fwd_split_workspace_bytes", "sparse_xattn_bwd",
            "sparse_xattn_bwd_workspace_bytes",
            "lse_combine", "chunk_cost", "lpt_assign", "context_gather", "sxa_last_error")
 
@@ -52,6 +53,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_xattn_fwd.restype = ctypes.c_int
     lib.sparse_xattn_fwd_workspace_bytes.argtypes = [I32, I32, I32]
     lib.sparse_xattn_fwd_workspace_bytes.restype = I64
+    lib.sparse_xattn_fwd_split_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.sparse_xattn_fwd_split_workspace_bytes.restype = I64
     lib.sparse_xattn_bwd.argtypes = attn_common + [P, P, P, P, P, P, P, P, P, P, I64, I32, P]
     lib.sparse_xattn_bwd_workspace_bytes.argtypes = [I32, I64, I32, I32, I32]
     lib.sparse_xattn_bwd_workspace_bytes.restype = I64
@@ -124,7 +127,9 @@ class Meta:
 def sparse_xattn_fwd(q, k, v, meta: Meta, scale: float, k_self=None, v_self=None,
                      out_dtype=None, out=None, lse=None, workspace="auto"):
     """Partial forward over the local chunks (+ own-block term).  Returns (o, lse).
-    ``workspace``: "auto" (cached scratch), None, or a device tensor."""
+    ``workspace``: "auto" (cached scratch: heaviest row groups dispatched first),
+    "split" (cached scratch of the split schedule: row groups with many key tiles
+    also run as several merged pieces), None, or a device tensor."""
     n_q, hq, d = q.shape
     hkv = k.shape[1]
     _need(q, "q", dtype=q.dtype)
@@ -143,10 +148,16 @@ def sparse_xattn_fwd(q, k, v, meta: Meta, scale: float, k_self=None, v_self=None
     _need(out, "out", (n_q, hq, d), out_dtype)
     _need(lse, "lse", (n_q, hq), torch.float32)
     lib = load_library()
-    if isinstance(workspace, str):  # "auto"
-        workspace = _scratch("fwd", int(lib.sparse_xattn_fwd_workspace_bytes(meta.n_blk, hq, hkv)),
-                             q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if isinstance(workspace, str):
+        if workspace not in ("auto", "split"):
+            raise ValueError(f"workspace must be 'auto', 'split', None or a tensor, not {workspace!r}")
+        with torch.cuda.device(q.device):
+            ws_bytes = int(lib.sparse_xattn_fwd_split_workspace_bytes(meta.n_blk, hq, hkv, d)
+                           if workspace == "split" else
+                           lib.sparse_xattn_fwd_workspace_bytes(meta.n_blk, hq, hkv))
+        workspace = _scratch("fwd_" + workspace, ws_bytes, q.device)
+    else:
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.sparse_xattn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), meta.n_blk, BLOCK, hq, hkv, d, float(scale),
         _ptr(meta.anchor), _ptr(meta.sample_start), _ptr(meta.chunk_gstart), _ptr(meta.chunk_len),

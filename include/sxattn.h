@@ -84,7 +84,13 @@ typedef enum {
  *   workspace, workspace_bytes: optional device scratch (at least
  *   sparse_xattn_fwd_workspace_bytes() bytes, else ignored).  With it the bf16 path
  *   first ranks its query row groups by the number of key tiles they read and
- *   dispatches the heaviest first; results do not depend on it.  Calls that share a
+ *   dispatches the heaviest first; results do not depend on it.  With at least
+ *   sparse_xattn_fwd_split_workspace_bytes() bytes the bf16 path also splits the key
+ *   tiles of every row group that reads more than 1.5 times the mean work of a
+ *   compute unit into pieces run by separate workgroups, whose partial O and lse a merge pass
+ *   combines exactly as lse_combine does ("Exchange the smaller side": partials with
+ *   their statistics merge into the unsplit result).  Results then agree with the
+ *   unsplit call up to float32 rounding, not bit for bit.  Calls that share a
  *   workspace must be ordered on one stream.
  * bf16 inputs run on bf16 MFMA with float32 accumulation and statistics; float32
  * inputs run in float32 throughout.
@@ -99,6 +105,12 @@ int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_d
 
 /* Workspace bytes of sparse_xattn_fwd's load balancing (0 for invalid sizes). */
 int64_t sparse_xattn_fwd_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv);
+
+/* Workspace bytes of sparse_xattn_fwd's split schedule (above) on the current device:
+ * the plan, and float32 partial O and lse for up to 2 * (compute units) pieces of 256
+ * query rows (about 67 MB at d = 128 on 256 compute units).  0 for invalid sizes and
+ * beyond 4096 row groups of 256 query rows per kv head, where no split is done. */
+int64_t sparse_xattn_fwd_split_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv, int32_t d);
 
 /* Phases of sparse_xattn_bwd (bit flags; 0 means all of DELTA | DQ | DKDV). */
 enum {

@@ -89,6 +89,19 @@ def test_dispatch_makespan():
     assert bench.dispatch_makespan([3, 3, 2, 2, 2], 2, 0) == 7   # greedy, longest first (the optimum is 6)
 
 
+
+def test_split_jobs():
+    # jobs at or under the cap stay whole; a longer one becomes equal pieces, each
+    # paying the merge
+    assert bench.split_jobs([4, 8], 8, 1) == [4, 8]
+    assert bench.split_jobs([20], 8, 1) == pytest.approx([20 / 3 + 1] * 3)
+    # one long job on many units: splitting shortens the makespan
+    assert bench.dispatch_makespan(bench.split_jobs([20, 1, 1, 1], 5, 1), 8, 0) == 6
+    # every unit already busy: the merges only add work
+    jobs = [10] * 16
+    assert bench.dispatch_makespan(bench.split_jobs(jobs, 5, 1), 8, 2) > bench.dispatch_makespan(jobs, 8, 2)
+
+
 def test_line_fit():
     x = np.array([1.0, 2.0, 3.0, 5.0])
     r2, worst = bench._fit(x, 2.0 + 3.0 * x)
