@@ -111,7 +111,7 @@ class Timers:
         return agg
 
 
-def build_problem(torch, seed, fwd_split=False):
+def build_problem(torch, seed, split=False):
     from block_sparse_cross_anchor_amd import synth, sxattn
 
     w = synth.WORKLOADS[WORKLOAD]
@@ -194,12 +194,13 @@ def build_problem(torch, seed, fwd_split=False):
             m.chunk_gstart, m.chunk_len = P["plan_gs"][b], P["plan_gl"][b]
             m.n_blk, m.n_chunk, m.n_loc = b1 - b0, per_bin, n_loc
             hm.append(m)
-        bws = int(lib.sparse_xattn_bwd_workspace_bytes(b1 - b0, n_loc, hq, hkv, d))
+        bws = int(lib.sparse_xattn_bwd_split_workspace_bytes(b1 - b0, n_loc, hq, hkv, d) if split
+                  else lib.sparse_xattn_bwd_workspace_bytes(b1 - b0, n_loc, hq, hkv, d))
         P["dq_halves"].append({
             "tok": slice(16 * b0, 16 * b1), "metas": hm,
             "delta": torch.empty((2, 16 * (b1 - b0), hq), dtype=f32, device="cuda"),
             "ws": torch.empty((max(bws, 256),), dtype=torch.uint8, device="cuda")})
-    fws = int(lib.sparse_xattn_fwd_split_workspace_bytes(w.n_anchor, hq, hkv, d) if fwd_split
+    fws = int(lib.sparse_xattn_fwd_split_workspace_bytes(w.n_anchor, hq, hkv, d) if split
               else lib.sparse_xattn_fwd_workspace_bytes(w.n_anchor, hq, hkv))
     P["fwd_ws"] = [torch.empty((max(fws, 256),), dtype=torch.uint8, device="cuda") for _ in range(2)]
     return P
@@ -511,6 +512,10 @@ def balance_study(torch, workload, seed, reps):
         "dq": lambda m: sxattn.sparse_xattn_bwd(q, k_loc, v_loc, m, scale, o, do, lse, dq,
                                                 delta_ws=delta, dk=dk, dv=dv,
                                                 flags=sxattn.BWD_DQ | sxattn.BWD_DQ_OVERWRITE),
+        "dq_split": lambda m: sxattn.sparse_xattn_bwd(q, k_loc, v_loc, m, scale, o, do, lse, dq,
+                                                      delta_ws=delta, dk=dk, dv=dv,
+                                                      flags=sxattn.BWD_DQ | sxattn.BWD_DQ_OVERWRITE,
+                                                      workspace="split"),
         "dkdv": lambda m: sxattn.sparse_xattn_bwd(q, k_loc, v_loc, m, scale, o, do, lse, dq,
                                                   delta_ws=delta, dk=dk, dv=dv,
                                                   flags=sxattn.BWD_DKDV),
@@ -541,7 +546,7 @@ def balance_study(torch, workload, seed, reps):
                 per[ph].append((e0, e1))
         torch.cuda.synchronize()
         ms = {ph: [e0.elapsed_time(e1) / reps for e0, e1 in per[ph]] for ph in phases}
-        tot = [sum(ms[ph][b] for ph in phases if ph != "fwd_split") for b in range(nb)]
+        tot = [sum(ms[ph][b] for ph in phases if not ph.endswith("_split")) for b in range(nb)]
         for b in range(nb):
             jobs = np.repeat(group_tiles[:, bins_np == b].sum(1), hkv)
             rows.append((name, b, {ph: ms[ph][b] for ph in phases}, tot[b],
@@ -558,7 +563,7 @@ def balance_study(torch, workload, seed, reps):
     out["contiguous_over_lpt_pairs"] = round(out["plans"]["contiguous"]["max_bin_ms"]
                                              / out["plans"]["lpt_pairs"]["max_bin_ms"], 3)
     fits = {}
-    for ph in [ph for ph in phases if ph != "fwd_split"] + ["total"]:
+    for ph in [ph for ph in phases if not ph.endswith("_split")] + ["total"]:
         y = [r[3] if ph == "total" else r[2][ph] for r in rows]
         fits[ph] = {}
         for pn in preds:
@@ -588,9 +593,12 @@ def balance_study(torch, workload, seed, reps):
                                     for r in lpt_rows) / base, 3)
             for cap in (8, 16, 32, 64)}
     out["split_measured"] = {
-        name: {"fwd_max_bin_ms": p["phase_max_ms"]["fwd"],
-               "fwd_split_max_bin_ms": p["phase_max_ms"]["fwd_split"],
-               "ratio": round(p["phase_max_ms"]["fwd_split"] / p["phase_max_ms"]["fwd"], 3)}
+        name: {ph: {"max_bin_ms": p["phase_max_ms"][ph],
+                    "split_max_bin_ms": p["phase_max_ms"][ph + "_split"],
+                    "ratio": round(p["phase_max_ms"][ph + "_split"] / p["phase_max_ms"][ph], 3),
+                    "mean_ratio": round(sum(p["per_bin_phase_ms"][ph + "_split"])
+                                        / sum(p["per_bin_phase_ms"][ph]), 3)}
+               for ph in ("fwd", "dq")}
         for name, p in out["plans"].items()}
     out["split_model_note"] = ("modelled max-bin time of the LPT plan with every row-group "
                                "job over cap tiles split into equal pieces (each paying the "
@@ -726,8 +734,8 @@ def main():
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fwd-split", action="store_true",
-                    help="run the step's forwards on the split schedule (split workspaces)")
+    ap.add_argument("--split", action="store_true",
+                    help="run the step's forwards and dQ phases on the split schedule")
     ap.add_argument("--balance", metavar="WORKLOAD",
                     help="instead of the benchmark, the per-bin balance study of a workload "
                          "with bins (fwd_bf16_8kq_64k or cp64_share_8kq_512k)")
@@ -765,7 +773,7 @@ def main():
         combine_study(torch, args.combine, args.seed, max(args.reps, 1))
         return
     log("building the synthetic workload ...")
-    P = build_problem(torch, args.seed, fwd_split=args.fwd_split)
+    P = build_problem(torch, args.seed, split=args.split)
     w = P["w"]
     T = Timers(torch)
     log(f"warmup {args.warmup} steps ...")
@@ -828,7 +836,7 @@ def main():
         "config": {"workload": WORKLOAD, "n_q": w.n_q, "n_ctx": w.n_ctx, "hq": w.hq,
                    "hkv": w.hkv, "head_dim": w.d, "block": 16, "chunks": w.n_chunk,
                    "chunk_size": w.chunk_size, "bins": w.n_bin, "seed": args.seed,
-                   "fwd_schedule": "split" if args.fwd_split else "ranked",
+                   "row_group_schedule": "split" if args.split else "ranked",
                    "allowed_pairs_per_head": pairs, "pct_of_bf16_peak": round(
                        100 * value / PEAK_BF16_TFLOPS, 2),
                    "lpt_imbalance": round(float(load.max() / load.mean() - 1), 5)},

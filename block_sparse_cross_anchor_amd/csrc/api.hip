@@ -116,13 +116,13 @@ int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_d
   if (workspace_bytes < 0) return fail(SXA_EINVAL, "workspace_bytes must be >= 0");
   const int64_t need = sparse_xattn_fwd_workspace_bytes(n_blk, hq, hkv);
   if (workspace != nullptr && need > 0 && workspace_bytes >= need) a.rg_order = static_cast<int32_t*>(workspace);
-  a.fwd_split = nullptr;
+  a.row_split = nullptr;
   a.n_cu = 0;
   if (workspace != nullptr && in_dtype == SXA_BF16) {
     const int32_t n_cu = sxa::n_compute_units();
-    const int64_t split = sxa::fwd_split_bytes(n_blk, hq, hkv, d, n_cu);
+    const int64_t split = sxa::row_split_bytes(n_blk, hq, hkv, d, n_cu);
     if (split > 0 && workspace_bytes >= split) {
-      a.fwd_split = workspace;
+      a.row_split = workspace;
       a.n_cu = n_cu;
     }
   }
@@ -169,6 +169,15 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
   const int64_t need = sxa::bwd_workspace_bytes(n_blk, n_loc, hq, hkv, d);
   a.workspace = (workspace != nullptr && need > 0 && workspace_bytes >= need) ? workspace : nullptr;
   a.workspace_bytes = workspace_bytes;
+  if (a.workspace != nullptr && in_dtype == SXA_BF16 && (flags & SXA_BWD_DQ)) {
+    const int32_t n_cu = sxa::n_compute_units();
+    const int64_t split = sxa::row_split_bytes(n_blk, hq, hkv, d, n_cu);
+    const int64_t base = (need + 255) / 256 * 256;
+    if (split > 0 && workspace_bytes >= base + split) {  // the split dQ schedule's plan and slots
+      a.row_split = static_cast<char*>(workspace) + base;
+      a.n_cu = n_cu;
+    }
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_blk == 0) {
     if (!(flags & SXA_BWD_DKDV)) return ok();
@@ -195,7 +204,15 @@ int64_t sparse_xattn_fwd_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv)
 
 int64_t sparse_xattn_fwd_split_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv, int32_t d) {
   if (n_blk < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || (d != 64 && d != 128)) return 0;
-  return sxa::fwd_split_bytes(n_blk, hq, hkv, d, sxa::n_compute_units());
+  return sxa::row_split_bytes(n_blk, hq, hkv, d, sxa::n_compute_units());
+}
+
+int64_t sparse_xattn_bwd_split_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hq, int32_t hkv, int32_t d) {
+  if (n_blk < 0 || n_loc < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || (d != 64 && d != 128)) return 0;
+  const int64_t need = sxa::bwd_workspace_bytes(n_blk, n_loc, hq, hkv, d);
+  const int64_t split = sxa::row_split_bytes(n_blk, hq, hkv, d, sxa::n_compute_units());
+  if (need <= 0 || split <= 0) return 0;
+  return (need + 255) / 256 * 256 + split;
 }
 
 int64_t sparse_xattn_bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hq, int32_t hkv, int32_t d) {

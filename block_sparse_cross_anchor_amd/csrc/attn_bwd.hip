@@ -62,6 +62,10 @@ struct BwdParams {
   float scale_log2;  // scale * log2(e)
   int32_t dq_overwrite;
   const int32_t* rg_order;  // dQ: row group of workgroup blockIdx / hkv (nullptr: identity)
+  // split dQ (jobs != nullptr): job blockIdx / hkv = {row group, first tile, end tile,
+  // slot}; a job with a slot writes its scaled dQ sum there instead of adding it
+  const int4* jobs;
+  float* part_dq;
 };
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
@@ -96,7 +100,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, h2 = lane / 32, l32 = lane % 32;
   const int g = blockIdx.x % p.hkv;
-  const int wg = p.rg_order ? p.rg_order[blockIdx.x / p.hkv] : static_cast<int>(blockIdx.x / p.hkv);
+  int wg, t_skip = 0, t_left = 0x7fffffff;
+  if (p.jobs) {
+    const int4 jb = p.jobs[blockIdx.x / p.hkv];
+    if (jb.x < 0) return;  // more job slots than jobs
+    wg = __builtin_amdgcn_readfirstlane(jb.x);  // uniform: kept in scalar registers
+    t_skip = __builtin_amdgcn_readfirstlane(jb.y);
+    t_left = __builtin_amdgcn_readfirstlane(jb.z - jb.y);
+  } else {
+    wg = p.rg_order ? p.rg_order[blockIdx.x / p.hkv] : static_cast<int>(blockIdx.x / p.hkv);
+  }
   const int grp = p.hq / p.hkv;
   const int64_t n_q = static_cast<int64_t>(p.n_blk) * kBlock;
   const int64_t R = n_q * grp;
@@ -111,8 +124,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
   }
   Walk w;
   w.start(p.k_self != nullptr, b_first, b_last);
+  // a piece of a split row group: skip to its first tile, stop after its last
+  Tile skipped;
+  for (int i = 0; i < t_skip; ++i) walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, skipped);
+  auto next_tile = [&](Tile& t) {
+    if (t_left == 0) return false;
+    --t_left;
+    return walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, t);
+  };
   Tile cur;
-  const bool have = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, cur);
+  const bool have = next_tile(cur);
 
   // this lane's query row (column of the 32-row N tile)
   const int64_t r = wg_row0 + 32 * wave + l32;
@@ -123,7 +144,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
   const int blk = static_cast<int>(tok / kBlock);
   const int64_t orow = tok * p.hq + static_cast<int64_t>(g) * grp + hh;
   if (!have) {  // no key of this call reaches these rows: nothing to add
-    if (p.dq_overwrite && valid) {
+    const int slot = p.jobs ? p.jobs[blockIdx.x / p.hkv].w : -1;  // re-read: not held in registers
+    if (slot >= 0) {  // (a piece always has tiles; an empty one adds zeros)
+      const int64_t pr = (static_cast<int64_t>(slot) * p.hkv + g) * ROWS + 32 * wave + l32;
+#pragma unroll
+      for (int d0 = h2 * (D / 2); d0 < (h2 + 1) * (D / 2); d0 += 4)
+        *reinterpret_cast<f32x4*>(p.part_dq + pr * D + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else if (p.dq_overwrite && valid) {
       // the two lanes of a row (h2 = 0, 1) each clear half of it
 #pragma unroll
       for (int d0 = h2 * (D / 2); d0 < (h2 + 1) * (D / 2); d0 += 4)
@@ -163,14 +190,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
   Tile n1, n2;
   const Dma dma(p.hkv, wave, lane);
   dma.issue(cur, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[0]));
-  bool have1 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n1);
+  bool have1 = next_tile(n1);
   if (have1) dma.issue(n1, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[1]));
   int cb = 0;
   while (true) {
     if (have1) wait_vmcnt<Dma::NI>();  // this wave's copies of `cur` landed (n1 may fly)
     else wait_vmcnt<0>();
     barrier_nofence();                 // ... and every wave's; all reads of the third buffer are done
-    const bool have2 = walk_next(w, p.chunk_gstart, p.chunk_len, p.n_chunk, LO, HI, n2);  // false once exhausted
+    const bool have2 = next_tile(n2);  // false once exhausted
     if (have2) dma.issue(n2, p.k, p.v, p.k_self, p.v_self, p.hkv, g, lane, lds_addr(bufs[cb == 0 ? 2 : cb - 1]));
 
     // per-lane constants are redefined opaquely per tile so that derived addresses
@@ -244,6 +271,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
   }
 
   if (!valid) return;
+  const int slot = p.jobs ? p.jobs[blockIdx.x / p.hkv].w : -1;  // re-read: not held in registers
+  if (slot >= 0) {  // a piece: its scaled sum to the slot (the merge adds the pieces)
+    const int64_t pr = (static_cast<int64_t>(slot) * p.hkv + g) * ROWS + 32 * wave + l32;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = p.scale * dqacc[dt][4 * jj + i];
+        *reinterpret_cast<f32x4*>(p.part_dq + pr * D + 32 * dt + 8 * jj + 4 * h2) = acc;
+      }
+    return;
+  }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -254,6 +295,34 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(p.scale, dqacc[dt][4 * jj + i], acc[i]);
       *reinterpret_cast<f32x4*>(dst) = acc;
     }
+}
+
+// Merge of a split row group's dQ pieces, one workgroup per (split group, kv head,
+// run of 256 / (d / 4) rows), d / 4 lanes per row: dq = (overwrite ? 0 : dq) + the
+// pieces' sums in piece order.  Workgroups of unused split-group entries return.
+template <int D>
+__global__ __launch_bounds__(256) void dq_merge_kernel(RowSplit sp, float* dq, int32_t n_blk, int32_t hq, int32_t hkv,
+                                                       int32_t overwrite) {
+  constexpr int LPR = D / 4;                 // lanes per row, 4 values each
+  constexpr int RPW = 256 / LPR;             // rows per workgroup
+  constexpr int RUNS = kRowsPerGroup / RPW;  // workgroups per (split group, kv head)
+  const int g = blockIdx.x % hkv;
+  const int run = (blockIdx.x / hkv) % RUNS;
+  const int4 jb = sp.groups[blockIdx.x / hkv / RUNS];
+  if (jb.x < 0) return;
+  const int grp = hq / hkv;
+  const int64_t R = static_cast<int64_t>(n_blk) * kBlock * grp;
+  const int sub = threadIdx.x % LPR;
+  const int lr = run * RPW + threadIdx.x / LPR;
+  const int64_t r = static_cast<int64_t>(jb.x) * kRowsPerGroup + lr;
+  if (r >= R) return;
+  const int64_t orow = (r / grp) * hq + static_cast<int64_t>(g) * grp + static_cast<int>(r % grp);
+  f32x4* dst = reinterpret_cast<f32x4*>(dq + orow * D + 4 * sub);
+  f32x4 acc = overwrite ? f32x4{0.f, 0.f, 0.f, 0.f} : *dst;
+  for (int k = 0; k < jb.z; ++k)
+    acc += *reinterpret_cast<const f32x4*>(
+        sp.part_o + ((static_cast<int64_t>(jb.y + k) * hkv + g) * kRowsPerGroup + lr) * D + 4 * sub);
+  *dst = acc;
 }
 
 // ============================================================================ dkdv kernel
@@ -953,18 +1022,34 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   p.scale_log2 = a.scale * kLog2e;
   p.dq_overwrite = (a.flags & SXA_BWD_DQ_OVERWRITE) != 0;
   p.rg_order = nullptr;
+  p.jobs = nullptr;
+  p.part_dq = nullptr;
   if (a.flags & SXA_BWD_DQ) {
     static_assert(32 * kDqWaves == kRowsPerGroup, "row groups are shared with the dispatch order");
     const int64_t groups = row_groups(a, kRowsPerGroup);
     const int64_t n_dq = groups * a.hkv;
-    if (a.workspace != nullptr && groups <= kMaxOrderedGroups) {
+    if (a.row_split != nullptr && groups <= kMaxOrderedGroups && groups > 0) {
+      const RowSplit sp = row_split_layout(a.row_split, a);
+      if ((e = launch_row_split_plan(a, sp, s)) != hipSuccess) return e;
+      p.jobs = sp.jobs;
+      p.part_dq = sp.part_o;
+      dq_bf16_kernel<D><<<dim3(static_cast<unsigned>((groups + sp.max_pieces) * a.hkv)), dim3(64 * kDqWaves), 0, s>>>(p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      constexpr int kRuns = kRowsPerGroup / (256 / (D / 4));
+      dq_merge_kernel<D><<<dim3(static_cast<unsigned>(sp.max_pieces / 2 * a.hkv * kRuns)), dim3(256), 0, s>>>(
+          sp, a.dq, a.n_blk, a.hq, a.hkv, p.dq_overwrite);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      p.jobs = nullptr;
+    } else if (a.workspace != nullptr && groups <= kMaxOrderedGroups) {
       const WsLayout L = ws_layout(a.n_blk, a.n_loc, D, a.hq / a.hkv);
       int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + L.order_off);
       if ((e = launch_row_group_order(a, kRowsPerGroup, order, s)) != hipSuccess) return e;
       p.rg_order = order;
     }
-    dq_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_dq)), dim3(64 * kDqWaves), 0, s>>>(p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.part_dq == nullptr) {
+      dq_bf16_kernel<D><<<dim3(static_cast<unsigned>(n_dq)), dim3(64 * kDqWaves), 0, s>>>(p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   if (!(a.flags & SXA_BWD_DKDV)) return hipSuccess;
   const int64_t n_ctx_tiles = (a.n_loc + kKeysPerWG - 1) / kKeysPerWG;

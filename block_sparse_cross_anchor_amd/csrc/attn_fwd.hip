@@ -417,7 +417,7 @@ fwd_bf16_kernel(FwdParams p) {
 constexpr int kMergeRowsPerLane = 1;
 
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdSplit sp, void* o, float* lse, int32_t n_blk, int32_t hq,
+__global__ __launch_bounds__(256) void fwd_merge_kernel(RowSplit sp, void* o, float* lse, int32_t n_blk, int32_t hq,
                                                         int32_t hkv) {
   constexpr int LPR = D / 4;                      // lanes per row, 4 values each
   constexpr int RPL = kMergeRowsPerLane;
@@ -513,9 +513,9 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   const int64_t groups = (rows + kRowsPerWG - 1) / kRowsPerWG;
   const int64_t n_wg = groups * a.hkv;
   if (n_wg == 0) return hipSuccess;
-  if (a.fwd_split != nullptr && groups <= kMaxOrderedGroups && kRowsPerWG == kRowsPerGroup) {
-    const FwdSplit sp = fwd_split_layout(a.fwd_split, a);
-    hipError_t e = launch_fwd_split_plan(a, sp, s);
+  if (a.row_split != nullptr && groups <= kMaxOrderedGroups && kRowsPerWG == kRowsPerGroup) {
+    const RowSplit sp = row_split_layout(a.row_split, a);
+    hipError_t e = launch_row_split_plan(a, sp, s);
     if (e != hipSuccess) return e;
     p.rg_order = nullptr;
     p.jobs = sp.jobs;

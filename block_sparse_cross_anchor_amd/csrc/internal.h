@@ -42,8 +42,8 @@ struct AttnArgs {
   void* workspace;  // optional dK/dV split scratch (nullptr: no split)
   int64_t workspace_bytes;
   int32_t* rg_order;  // optional scratch for the row-group dispatch order (nullptr: index order)
-  void* fwd_split;    // optional scratch of the split forward (nullptr: one workgroup per row group)
-  int32_t n_cu;       // compute units of the device (used with fwd_split)
+  void* row_split;    // optional scratch of the split forward or dQ phase (nullptr: one workgroup per row group)
+  int32_t n_cu;       // compute units of the device (used with row_split)
 };
 
 // Query rows per forward / dQ workgroup, and the largest row-group count that is
@@ -57,28 +57,30 @@ int n_compute_units();
 // when there are more than kMaxOrderedGroups groups).
 hipError_t launch_row_group_order(const AttnArgs& a, int rows_per_group, int32_t* order, hipStream_t s);
 
-// Split forward: a row group whose key tiles exceed the cap (1.5 times the mean tiles
-// per compute unit, at least kMinSplitTiles) runs as equal pieces of its tile walk, each
-// on its own workgroup; the pieces' partial O and lse go to slots, and a merge pass
-// writes the group's rows.  The plan lives in the caller's scratch:
-struct FwdSplit {
+// Split schedule of the forward and of the dQ phase: a row group whose key tiles
+// exceed the cap (1.5 times the mean tiles per compute unit, at least kMinSplitTiles)
+// runs as equal pieces of its tile walk, each on its own workgroup; the pieces'
+// partial results go to slots, and a merge pass writes the group's rows.  The plan
+// lives in the caller's scratch:
+struct RowSplit {
   int4* jobs;       // [n_groups + max_pieces]: {row group, first tile, end tile, slot or -1},
                     // most tiles first; row group -1: no job
   int4* groups;     // [max_pieces / 2]: {row group, first slot, pieces, 0}; row group -1: none
-  float* part_lse;  // [max_pieces][hkv][kRowsPerGroup] natural-log lse of each piece
-  float* part_o;    // [max_pieces][hkv][kRowsPerGroup][d] normalised partial O
+  float* part_lse;  // [max_pieces][hkv][kRowsPerGroup] forward: natural-log lse of each piece
+  float* part_o;    // [max_pieces][hkv][kRowsPerGroup][d] forward: normalised partial O;
+                    // dQ phase: the piece's scaled dQ sum
   int32_t max_pieces;
 };
 constexpr int kMinSplitTiles = 16;
 // Pieces of split row groups per kv head: the cap is above the mean tiles per compute
 // unit, so they never exceed 2 n_cu / hkv.
-int32_t fwd_split_max_pieces(int32_t hkv, int32_t n_cu);
+int32_t row_split_max_pieces(int32_t hkv, int32_t n_cu);
 // Bytes of the split forward's scratch (0 if not representable or beyond the
 // ordered-group limit).
-int64_t fwd_split_bytes(int32_t n_blk, int32_t hq, int32_t hkv, int32_t d, int32_t n_cu);
-FwdSplit fwd_split_layout(void* ws, const AttnArgs& a);
+int64_t row_split_bytes(int32_t n_blk, int32_t hq, int32_t hkv, int32_t d, int32_t n_cu);
+RowSplit row_split_layout(void* ws, const AttnArgs& a);
 // The plan of the split forward into sp (one workgroup).
-hipError_t launch_fwd_split_plan(const AttnArgs& a, const FwdSplit& sp, hipStream_t s);
+hipError_t launch_row_split_plan(const AttnArgs& a, const RowSplit& sp, hipStream_t s);
 
 // Bytes of dK/dV split scratch for n_loc local rows (0 if not representable).
 int64_t bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hq, int32_t hkv, int32_t d);

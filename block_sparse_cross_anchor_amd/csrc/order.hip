@@ -125,7 +125,7 @@ constexpr int kLenBuckets = 1024;  // piece lengths are ranked exactly up to thi
 // in any order; buckets of cap / kLenBuckets tiles when cap exceeds kLenBuckets), so
 // dispatch in index order is longest-first.  Pieces of split groups get consecutive
 // slots in group order.  Every pass is parallel over groups or length buckets.
-__global__ __launch_bounds__(kOrderThreads) void fwd_split_plan_kernel(AttnArgs a, int n_groups, FwdSplit sp) {
+__global__ __launch_bounds__(kOrderThreads) void row_split_plan_kernel(AttnArgs a, int n_groups, RowSplit sp) {
   __shared__ int cost[kMaxOrderedGroups];
   __shared__ int pieces[kMaxOrderedGroups];
   __shared__ int slot[kMaxOrderedGroups], sidx[kMaxOrderedGroups];  // (interval arrays first)
@@ -206,7 +206,7 @@ int n_compute_units() {
   return n;
 }
 
-int32_t fwd_split_max_pieces(int32_t hkv, int32_t n_cu) { return max(2, (2 * n_cu + hkv - 1) / hkv); }
+int32_t row_split_max_pieces(int32_t hkv, int32_t n_cu) { return max(2, (2 * n_cu + hkv - 1) / hkv); }
 
 namespace {
 struct SplitLayout {
@@ -224,21 +224,21 @@ SplitLayout split_layout(int64_t groups, int64_t hkv, int64_t d, int64_t pieces)
 }
 }  // namespace
 
-int64_t fwd_split_bytes(int32_t n_blk, int32_t hq, int32_t hkv, int32_t d, int32_t n_cu) {
+int64_t row_split_bytes(int32_t n_blk, int32_t hq, int32_t hkv, int32_t d, int32_t n_cu) {
   AttnArgs a;
   a.n_blk = n_blk;
   a.hq = hq;
   a.hkv = hkv;
   const int64_t groups = row_groups(a, kRowsPerGroup);
   if (groups <= 0 || groups > kMaxOrderedGroups) return 0;
-  return split_layout(groups, hkv, d, fwd_split_max_pieces(hkv, n_cu)).bytes;
+  return split_layout(groups, hkv, d, row_split_max_pieces(hkv, n_cu)).bytes;
 }
 
-FwdSplit fwd_split_layout(void* ws, const AttnArgs& a) {
-  const int32_t pieces = fwd_split_max_pieces(a.hkv, a.n_cu);
+RowSplit row_split_layout(void* ws, const AttnArgs& a) {
+  const int32_t pieces = row_split_max_pieces(a.hkv, a.n_cu);
   const SplitLayout L = split_layout(row_groups(a, kRowsPerGroup), a.hkv, a.d, pieces);
   char* b = static_cast<char*>(ws);
-  FwdSplit sp;
+  RowSplit sp;
   sp.jobs = reinterpret_cast<int4*>(b + L.jobs_off);
   sp.groups = reinterpret_cast<int4*>(b + L.groups_off);
   sp.part_lse = reinterpret_cast<float*>(b + L.lse_off);
@@ -247,10 +247,10 @@ FwdSplit fwd_split_layout(void* ws, const AttnArgs& a) {
   return sp;
 }
 
-hipError_t launch_fwd_split_plan(const AttnArgs& a, const FwdSplit& sp, hipStream_t s) {
+hipError_t launch_row_split_plan(const AttnArgs& a, const RowSplit& sp, hipStream_t s) {
   const int64_t n = row_groups(a, kRowsPerGroup);
   if (n <= 0 || n > kMaxOrderedGroups) return hipErrorInvalidValue;
-  fwd_split_plan_kernel<<<dim3(1), dim3(kOrderThreads), 0, s>>>(a, static_cast<int>(n), sp);
+  row_split_plan_kernel<<<dim3(1), dim3(kOrderThreads), 0, s>>>(a, static_cast<int>(n), sp);
   return hipGetLastError();
 }
 

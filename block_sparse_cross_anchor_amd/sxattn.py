@@ -24,7 +24,7 @@ BLOCK = 16
 
 EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_fwd_workspace_bytes",
            "sparse_xattn_fwd_split_workspace_bytes", "sparse_xattn_bwd",
-           "sparse_xattn_bwd_workspace_bytes",
+           "sparse_xattn_bwd_workspace_bytes", "sparse_xattn_bwd_split_workspace_bytes",
            "lse_combine", "chunk_cost", "lpt_assign", "context_gather", "sxa_last_error")
 
 _lib = None
@@ -58,6 +58,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.sparse_xattn_bwd.argtypes = attn_common + [P, P, P, P, P, P, P, P, P, P, I64, I32, P]
     lib.sparse_xattn_bwd_workspace_bytes.argtypes = [I32, I64, I32, I32, I32]
     lib.sparse_xattn_bwd_workspace_bytes.restype = I64
+    lib.sparse_xattn_bwd_split_workspace_bytes.argtypes = [I32, I64, I32, I32, I32]
+    lib.sparse_xattn_bwd_split_workspace_bytes.restype = I64
     lib.sparse_xattn_bwd.restype = ctypes.c_int
     lib.lse_combine.argtypes = [P, ctypes.c_int, P, I32, I64, I32, P, ctypes.c_int, P, P]
     lib.lse_combine.restype = ctypes.c_int
@@ -180,19 +182,23 @@ def _scratch(kind: str, need: int, device) -> torch.Tensor:
     return ws
 
 
-def bwd_workspace(n_blk: int, n_loc: int, hq: int, hkv: int, d: int, device) -> torch.Tensor:
-    """Scratch of the load-balanced dQ and dK/dV phases (cached per device)."""
+def bwd_workspace(n_blk: int, n_loc: int, hq: int, hkv: int, d: int, device, split=False):
+    """Scratch of the load-balanced dQ and dK/dV phases (cached per device), with the
+    split dQ schedule's plan and slots when ``split``.  Returns (tensor, bytes to pass)."""
+    lib = load_library()
+    size = lib.sparse_xattn_bwd_split_workspace_bytes if split else lib.sparse_xattn_bwd_workspace_bytes
     with torch.cuda.device(torch.device(device)):
-        need = int(load_library().sparse_xattn_bwd_workspace_bytes(int(n_blk), int(n_loc), int(hq),
-                                                                    int(hkv), int(d)))
-    return _scratch("bwd", need, device)
+        need = int(size(int(n_blk), int(n_loc), int(hq), int(hkv), int(d)))
+    return _scratch("bwd_split" if split else "bwd", need, device), need
 
 
 def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
                      k_self=None, v_self=None, delta_ws=None, dk=None, dv=None, dk_self=None,
                      dv_self=None, flags: int = 0, workspace="auto"):
     """Backward of the local chunks (+ own-block term).  Adds into dq_accum (float32)
-    unless BWD_DQ_OVERWRITE is set; ``flags`` selects phases (0 = all).
+    unless BWD_DQ_OVERWRITE is set; ``flags`` selects phases (0 = all).  ``workspace``:
+    "auto" (cached scratch: load-balanced phases), "split" (also the split dQ
+    schedule), None, or a device tensor.
     Returns the float32 gradients (dk, dv, dk_self, dv_self)."""
     n_q, hq, d = q.shape
     hkv = k.shape[1]
@@ -223,9 +229,13 @@ def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
         _need(dk_self, "dk_self", k_self.shape, f32)
         _need(dv_self, "dv_self", v_self.shape, f32)
     lib = load_library()
-    if isinstance(workspace, str):  # "auto"
-        workspace = bwd_workspace(meta.n_blk, meta.n_loc, hq, hkv, d, q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if isinstance(workspace, str):
+        if workspace not in ("auto", "split"):
+            raise ValueError(f"workspace must be 'auto', 'split', None or a tensor, not {workspace!r}")
+        workspace, ws_bytes = bwd_workspace(meta.n_blk, meta.n_loc, hq, hkv, d, q.device,
+                                            split=workspace == "split")
+    else:
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.sparse_xattn_bwd(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), meta.n_blk, BLOCK, hq, hkv, d, float(scale),
         _ptr(meta.anchor), _ptr(meta.sample_start), _ptr(meta.chunk_gstart), _ptr(meta.chunk_len),

@@ -139,8 +139,15 @@ enum {
  *            load-balanced: one workgroup per compute unit, each taking an equal
  *            share of all (key tile, query step) work, with the partial sums of
  *            tiles split between workgroups added by a second pass.  With NULL (or
- *            too small) every 256-key tile is handled by one workgroup.  Contents
- *            are scratch; calls that share a workspace must be ordered on one stream.
+ *            too small) every 256-key tile is handled by one workgroup.  With at
+ *            least sparse_xattn_bwd_split_workspace_bytes() bytes the bf16 dQ phase
+ *            also runs the split schedule of sparse_xattn_fwd: query row groups that
+ *            read more than 1.5 times the mean work of a compute unit are cut into
+ *            pieces of their key tiles, each piece's dQ sum goes to a slot, and a
+ *            second pass adds the pieces to dq_accum (dQ is a plain sum over keys,
+ *            "Exchange the smaller side"); results then agree with the unsplit phase
+ *            up to float32 summation order.  Contents are scratch; calls that share
+ *            a workspace must be ordered on one stream.
  *   flags    SXA_BWD_* bits selecting the phases; they run in the order
  *            DELTA, DQ, DKDV on `stream`.
  */
@@ -159,6 +166,13 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
  * 0 for invalid sizes). */
 int64_t sparse_xattn_bwd_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hq, int32_t hkv,
                                          int32_t d);
+
+/* Workspace bytes for the same phases with the split dQ schedule (above) on the
+ * current device: sparse_xattn_bwd_workspace_bytes() rounded up to 256, plus the plan
+ * and float32 slots of up to 2 * (compute units) pieces of 256 query rows.  0 for
+ * invalid sizes and beyond 4096 row groups of 256 query rows per kv head. */
+int64_t sparse_xattn_bwd_split_workspace_bytes(int32_t n_blk, int64_t n_loc, int32_t hq, int32_t hkv,
+                                               int32_t d);
 
 /*
  * Exact merge of n_parts partials from their log-sum-exp statistics

@@ -171,3 +171,71 @@ def test_split_workspace_reused_by_a_smaller_call_and_no_key_calls():
                                          inp2.v_self.f64 if with_self else None)
         assert rel_frob(host64(o), ro) <= 1e-2 if ro.any() else not host64(o).any()
         assert_lse_close(host64(lse), rl, 1e-3)
+
+
+def draw_case(case):
+    n_ctx, lo, hi, n_blk, hq, hkv, d, kind, with_self = CASES[case]
+    seed = 40 + case
+    meta = synth.draw_meta(seed, n_ctx, lo, hi, n_blk)
+    if kind == "contiguous":
+        gs, gl = synth.contiguous_chunks(n_ctx, 1024)
+    else:
+        rng = np.random.default_rng(seed)
+        cuts = np.sort(rng.choice(np.arange(1, n_ctx), 9, replace=False))
+        starts = np.concatenate([[0], cuts]).astype(np.int32)
+        lens = np.diff(np.concatenate([starts, [n_ctx]])).astype(np.int32)
+        keep = rng.permutation(len(starts))[:8]
+        gs, gl = starts[keep], lens[keep]
+    inp = synth.draw_inputs(seed, meta, hq, hkv, d, "bf16", 1.0, gs, gl, self_block=with_self,
+                            with_dout=True)
+    return meta, inp, gs, gl, hq, hkv, d, with_self
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_split_dq_matches_unsplit_and_oracle(case):
+    """The dQ phase on the split schedule: the same sums as the unsplit phase up to
+    float32 summation order, accumulating into dq_accum or overwriting it; against the
+    oracle (each side from its own forward) on the first two cases."""
+    meta, inp, gs, gl, hq, hkv, d, with_self = draw_case(case)
+    scale = 1.0 / math.sqrt(d)
+    dm = device_meta(meta, gs, gl)
+    q, k, v, do = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.dout)
+    ks = dev(inp.k_self) if with_self else None
+    vs = dev(inp.v_self) if with_self else None
+    o, lse = sxattn.sparse_xattn_fwd(q, k, v, dm, scale, ks, vs, workspace=None)
+    delta = torch.empty((2,) + tuple(lse.shape), dtype=torch.float32, device="cuda")
+    scratch_dq = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+    sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o, do, lse, scratch_dq, ks, vs, delta_ws=delta,
+                            flags=sxattn.BWD_DELTA, workspace=None)
+    init = torch.randn(q.shape, generator=torch.Generator().manual_seed(case)).cuda()
+    out = {}
+    for ws in ("auto", "split"):
+        for mode, flags in (("acc", sxattn.BWD_DQ), ("over", sxattn.BWD_DQ | sxattn.BWD_DQ_OVERWRITE)):
+            dq = init.clone()
+            sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o, do, lse, dq, ks, vs, delta_ws=delta,
+                                    flags=flags, workspace=ws)
+            out[ws, mode] = dq
+    torch.cuda.synchronize()
+    # the split call left its plan at the start of the scratch's split region
+    need = int(sxattn.load_library().sparse_xattn_bwd_workspace_bytes(meta.n_blk, int(gl.sum()), hq,
+                                                                        hkv, d))
+    base = -(-need // 256) * 256
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    pieces = max(2, -(-2 * n_cu // hkv))
+    tiles = group_tiles(meta, hq, hkv, gs, gl, with_self)
+    ws = sxattn._workspaces[("bwd_split", torch.device("cuda", torch.cuda.current_device()))]
+    jobs = ws[base:base + 16 * (len(tiles) + pieces)].cpu().numpy().view(np.int32).reshape(-1, 4)
+    assert check_plan(jobs, pieces, tiles) > 0
+    dq_u = host64(out["auto", "over"])
+    assert np.abs(dq_u).max() > 0
+    assert rel_frob(host64(out["split", "over"]), dq_u) <= 1e-5
+    assert rel_frob(host64(out["split", "acc"]) - host64(init), dq_u) <= 1e-5
+    assert rel_frob(host64(out["split", "acc"]), host64(out["auto", "acc"])) <= 1e-6
+    if case < 2:
+        ks64 = inp.k_self.f64 if with_self else None
+        vs64 = inp.v_self.f64 if with_self else None
+        ro, rl = oracle.sparse_xattn_fwd(inp.q.f64, inp.k.f64, inp.v.f64, meta.anchor,
+                                         meta.sample_start, gs, gl, scale, ks64, vs64)
+        r = oracle.sparse_xattn_bwd(inp.q.f64, inp.k.f64, inp.v.f64, ro, inp.dout.f64, rl,
+                                    meta.anchor, meta.sample_start, gs, gl, scale, ks64, vs64)
+        assert rel_frob(host64(out["split", "over"]), r[0]) <= 3e-2

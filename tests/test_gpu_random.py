@@ -4,7 +4,8 @@ Each seeded case draws the number of blocks, the packed context (sample lengths 
 anchors), the head layout (Hq, Hkv), the head dimension, the dtype and a chunk list:
 a random subset of a random partition of the context (ragged lengths, chunks of one
 token, chunks listed out of order), with or without the own-block term and with or
-without the load-balancing workspaces (in the forward also the split schedule).  Values are N(0, 1), so the softmax is peaked
+without the load-balancing workspaces (also with the split schedule of the forward
+and dQ phases).  Values are N(0, 1), so the softmax is peaked
 and a wrong mask or scale shows.  The forward, the split-then-combine of one call per
 chunk, and the backward (each side end to end: GPU forward then GPU backward, oracle
 forward then oracle backward) are compared with the oracle at the usual tolerances.
@@ -93,7 +94,7 @@ def test_random_case(seed):
     o_in, l_in = sxattn.sparse_xattn_fwd(q, k, v, dm, scale, ks, vs, workspace=ws)
     dq = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
     dk, dv, dks, dvs = sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o_in, do, l_in, dq, ks, vs,
-                                               workspace="auto" if ws == "split" else ws)
+                                               workspace=ws)
     torch.cuda.synchronize()
     r = oracle.sparse_xattn_bwd(inp.q.f64, inp.k.f64, inp.v.f64, ro, inp.dout.f64, rl,
                                 meta.anchor, meta.sample_start, gs, gl, scale, ks64, vs64)
