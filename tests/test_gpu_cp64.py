@@ -11,8 +11,9 @@ chunks are the local shard.  On it:
     interval meets none of that bin's chunks);
   * the backward of the shard from the combined O and lse: dQ and the own-block
     dK, dV of sampled blocks, and dK, dV of 64-key windows of the shard.
-The combine and the backward take the combined values only for the blocks that
-are checked (sampled blocks and the readers of the windows; rows are independent),
+The split schedule (forward and dQ) is compared with the default schedule on the
+whole share.  The combine and the backward take the combined values only for the
+blocks that are checked (sampled blocks and the readers of the windows; rows are independent),
 and every other row keeps the shard's own partial.  The oracle's side is its own:
 its forward of those blocks, its combine with the same synthetic partials, its
 backward from that.
@@ -51,9 +52,14 @@ def test_cp64_bin0_share_forward_combine_backward_sampled():
     q, k, v, ks, vs, do = (dev(t) for t in (inp.q, inp.k, inp.v, inp.k_self, inp.v_self, inp.dout))
     dm = device_meta(meta, gs, gl)
 
-    # ---- partial forward of the shard
+    # ---- partial forward of the shard; the split schedule on the whole share agrees
+    # with it to the bf16 rounding of P
     o_p, l_p = sxattn.sparse_xattn_fwd(q, k, v, dm, scale, ks, vs)
+    o_s, l_s = sxattn.sparse_xattn_fwd(q, k, v, dm, scale, ks, vs, workspace="split")
     torch.cuda.synchronize()
+    assert rel_frob(host64(o_s), host64(o_p)) <= 4e-3
+    assert_lse_close(host64(l_s), host64(l_p), 1e-5)
+    del o_s, l_s
 
     # blocks to check: first and last, blocks whose interval meets the shard, and the
     # readers of three 64-key windows of the shard
@@ -107,7 +113,12 @@ def test_cp64_bin0_share_forward_combine_backward_sampled():
     dq = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
     dk, dv, dks, dvs = sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o_in.view(n_q, hq, d), do,
                                                l_in.view(n_q, hq), dq, ks, vs)
+    dq_s = torch.zeros(q.shape, dtype=torch.float32, device="cuda")   # dQ on the split schedule
+    sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o_in.view(n_q, hq, d), do, l_in.view(n_q, hq), dq_s,
+                            ks, vs, flags=sxattn.BWD_DELTA | sxattn.BWD_DQ, workspace="split")
     torch.cuda.synchronize()
+    assert rel_frob(host64(dq_s), host64(dq)) <= 1e-5
+    del dq_s
     ro_f = ro_f.reshape(-1, hq, d)
     rl_f = rl_f.reshape(-1, hq)
 
