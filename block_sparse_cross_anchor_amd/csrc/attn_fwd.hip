@@ -434,26 +434,29 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(RowSplit sp, void* o, fl
 #pragma unroll
   for (int i = 0; i < RPL; ++i) lr[i] = run * RPW + i * (256 / LPR) + threadIdx.x / LPR;  // < kRowsPerGroup
   auto prow = [&](int k, int i) { return (static_cast<int64_t>(jb.y + k) * hkv + g) * kRowsPerGroup + lr[i]; };
-  float mx[RPL];
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) mx[i] = -INFINITY;
-  for (int k = 0; k < jb.z; ++k)
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) mx[i] = fmaxf(mx[i], sp.part_lse[prow(k, i)]);
+  // one pass over the pieces with a running maximum, so each piece's lse and O are
+  // loaded together: den and acc are rescaled when the maximum grows
+  float mx[RPL], den[RPL];
   f32x4 acc[RPL];
-  float den[RPL];
 #pragma unroll
   for (int i = 0; i < RPL; ++i) {
-    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mx[i] = -INFINITY;
     den[i] = 0.f;
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+#pragma unroll 2
   for (int k = 0; k < jb.z; ++k)
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      // exp(-inf) = 0; a row with every piece at -inf keeps den = 0
-      const float wk = mx[i] == -INFINITY ? 0.f : expf(sp.part_lse[prow(k, i)] - mx[i]);
-      den[i] += wk;
-      acc[i] += wk * *reinterpret_cast<const f32x4*>(sp.part_o + prow(k, i) * D + 4 * sub);
+      const float lk = sp.part_lse[prow(k, i)];
+      const f32x4 ok = *reinterpret_cast<const f32x4*>(sp.part_o + prow(k, i) * D + 4 * sub);
+      if (lk == -INFINITY) continue;  // an empty piece adds nothing
+      const float mnew = fmaxf(mx[i], lk);
+      const float c = expf(mx[i] - mnew);  // 0 while mx is -inf
+      const float wk = expf(lk - mnew);
+      den[i] = den[i] * c + wk;
+      acc[i] = acc[i] * c + wk * ok;
+      mx[i] = mnew;
     }
 #pragma unroll
   for (int i = 0; i < RPL; ++i) {
