@@ -7,6 +7,8 @@
 // DIR/{gs,gl}.bin          int32 [n_chunk]: the local chunk list (global start, length)
 // DIR/{q,ks,vs}.bin        bf16 bits [16 n_blk][hq | hkv][d]
 // DIR/{k,v}.bin            bf16 bits [sum gl][hkv][d]: the listed chunks back to back
+// DIR/dout.bin             bf16 bits [16 n_blk][hq][d]
+// DIR/{ggs,ggl}.bin        int32 [2]: two row ranges of k for the gather
 // Writes:
 // DIR/cost.bin   int64 [ceil(n_ctx / chunk_size)]   chunk_cost over the whole context
 // DIR/bins.bin   int32, DIR/load.bin int64          lpt_assign of those costs onto n_bin
@@ -15,6 +17,9 @@
 // DIR/o2.bin, DIR/lse2.bin                          the same from two calls (first half of the
 //                                                   chunks with the own-block term, then the
 //                                                   rest) merged by lse_combine
+// DIR/kg.bin     bf16 bits                          context_gather of the two k row ranges
+// DIR/{dq,dk,dv,dks,dvs}.bin float32                 sparse_xattn_bwd (all phases, dq
+//                                                   overwritten, load-balanced) from o, lse
 // Exit status 0 on success; on a library error it prints sxa_last_error().
 #include <hip/hip_runtime_api.h>
 
@@ -93,6 +98,9 @@ int run(const std::string& dir) {
   const auto vs = read_file<uint16_t>(dir + "/vs.bin", n_q * hkv * d);
   const auto k = read_file<uint16_t>(dir + "/k.bin", n_loc * hkv * d);
   const auto v = read_file<uint16_t>(dir + "/v.bin", n_loc * hkv * d);
+  const auto dout = read_file<uint16_t>(dir + "/dout.bin", n_q * hq * d);
+  const auto ggs = read_file<int32_t>(dir + "/ggs.bin", 2);
+  const auto ggl = read_file<int32_t>(dir + "/ggl.bin", 2);
 
   Dev<int32_t> d_anchor(anchor), d_start(start), d_gs(gs), d_gl(gl);
   Dev<uint16_t> d_q(q), d_ks(ks), d_vs(vs), d_k(k), d_v(v);
@@ -160,6 +168,34 @@ int run(const std::string& dir) {
   hip_check(hipStreamSynchronize(s), "sync");
   write_file(dir + "/o2.bin", d_o2.host());
   write_file(dir + "/lse2.bin", d_lse2.host());
+
+  // context_gather: two row ranges of k (rows of hkv * d bf16) back to back
+  Dev<int32_t> d_ggs(ggs), d_ggl(ggl);
+  const int64_t n_g = static_cast<int64_t>(ggl[0]) + ggl[1];
+  Dev<uint16_t> d_kg(n_g * hkv * d);
+  sxa_check(context_gather(d_k.p, hkv * d * 2, d_ggs.p, d_ggl.p, 2, n_g, d_kg.p, s), "context_gather");
+  hip_check(hipStreamSynchronize(s), "sync");
+  write_file(dir + "/kg.bin", d_kg.host());
+
+  // backward of every listed chunk with the own-block term, from the forward's O and lse
+  Dev<uint16_t> d_do(dout);
+  Dev<float> d_delta(2 * rows), d_dq(rows * d), d_dk(n_loc * hkv * d), d_dv(n_loc * hkv * d);
+  Dev<float> d_dks(n_q * hkv * d), d_dvs(n_q * hkv * d);
+  Dev<uint8_t> d_bws(static_cast<size_t>(sparse_xattn_bwd_workspace_bytes(
+      static_cast<int32_t>(n_blk), n_loc, static_cast<int32_t>(hq), static_cast<int32_t>(hkv), static_cast<int32_t>(d))));
+  sxa_check(sparse_xattn_bwd(d_q.p, d_k.p, d_v.p, SXA_BF16, static_cast<int32_t>(n_blk), 16,
+                             static_cast<int32_t>(hq), static_cast<int32_t>(hkv), static_cast<int32_t>(d), scale,
+                             d_anchor.p, d_start.p, d_gs.p, d_gl.p, static_cast<int32_t>(n_chunk), n_loc, d_ks.p,
+                             d_vs.p, d_o.p, d_do.p, d_lse.p, d_delta.p, d_dq.p, d_dk.p, d_dv.p, d_dks.p, d_dvs.p,
+                             d_bws.p, static_cast<int64_t>(d_bws.n),
+                             SXA_BWD_DELTA | SXA_BWD_DQ | SXA_BWD_DKDV | SXA_BWD_DQ_OVERWRITE, s),
+            "sparse_xattn_bwd");
+  hip_check(hipStreamSynchronize(s), "sync");
+  write_file(dir + "/dq.bin", d_dq.host());
+  write_file(dir + "/dk.bin", d_dk.host());
+  write_file(dir + "/dv.bin", d_dv.host());
+  write_file(dir + "/dks.bin", d_dks.host());
+  write_file(dir + "/dvs.bin", d_dvs.host());
   hip_check(hipStreamDestroy(s), "hipStreamDestroy");
   return 0;
 }

@@ -1,8 +1,11 @@
 """The C ABI alone: a plain host program (tests/c_abi/sxattn_c_driver.cpp, built by
-build()) calls chunk_cost, lpt_assign, sparse_xattn_fwd and lse_combine on HIP device
-buffers it allocates itself, with no Python or PyTorch in the process.  Its outputs are
-compared with the oracle: costs and the plan bit-exact; the forward (with the own-block
-term) and the two-call split merged by the combine at the bf16 tolerances.
+build()) calls chunk_cost, lpt_assign, sparse_xattn_fwd, lse_combine, context_gather
+and sparse_xattn_bwd on HIP device buffers it allocates itself, with no Python or
+PyTorch in the process.  Its outputs are compared with the oracle: costs and the plan
+bit-exact, the gather bit-exact against slicing; the forward (with the own-block
+term) and the two-call split merged by the combine at the bf16 tolerances; the
+backward (from the driver's own forward; the oracle's from the oracle's forward) at
+the gradient tolerance.
 """
 
 import math
@@ -37,15 +40,19 @@ def test_c_driver_matches_oracle(tmp_path, seed, order):
     if order == "shuffled":   # chunks listed out of order, one of them split unevenly
         gs = np.array([3072, 1024, 0, 2048, 2560], np.int32)
         gl = np.array([1024, 1024, 1024, 512, 512], np.int32)
-    inp = synth.draw_inputs(seed, meta, w.hq, w.hkv, w.d, "bf16", w.std(), gs, gl)
+    inp = synth.draw_inputs(seed, meta, w.hq, w.hkv, w.d, "bf16", w.std(), gs, gl, with_dout=True)
     n_bin = 2
     d = tmp_path
     (d / "args.txt").write_text(f"{meta.n_blk} {w.hq} {w.hkv} {w.d} {w.n_ctx} {w.chunk_size} "
                                 f"{n_bin} {len(gs)}\n")
     for name, arr in (("anchor", meta.anchor), ("start", meta.sample_start), ("gs", gs), ("gl", gl)):
         np.ascontiguousarray(arr, np.int32).tofile(d / f"{name}.bin")
-    for name, t in (("q", inp.q), ("ks", inp.k_self), ("vs", inp.v_self), ("k", inp.k), ("v", inp.v)):
+    for name, t in (("q", inp.q), ("ks", inp.k_self), ("vs", inp.v_self), ("k", inp.k), ("v", inp.v),
+                    ("dout", inp.dout)):
         np.ascontiguousarray(t.bits).tofile(d / f"{name}.bin")
+    ggs, ggl = np.array([1500, 37], np.int32), np.array([700, 1000], np.int32)
+    ggs.tofile(d / "ggs.bin")
+    ggl.tofile(d / "ggl.bin")
     r = subprocess.run([DRIVER, str(d)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
 
@@ -65,3 +72,14 @@ def test_c_driver_matches_oracle(tmp_path, seed, order):
         lse = np.fromfile(d / f"{l_name}.bin", np.float32).astype(np.float64).reshape(rl.shape)
         assert np.abs(o - ro).max() <= 2e-2 and rel_frob(o, ro) <= 1e-2, o_name
         assert_lse_close(lse, rl, 1e-3)
+
+    kg = np.fromfile(d / "kg.bin", np.uint16).reshape(-1, w.hkv, w.d)
+    kbits = np.ascontiguousarray(inp.k.bits)
+    np.testing.assert_array_equal(kg, np.concatenate([kbits[1500:2200], kbits[37:1037]]))
+
+    r = oracle.sparse_xattn_bwd(inp.q.f64, inp.k.f64, inp.v.f64, ro, inp.dout.f64, rl,
+                                meta.anchor, meta.sample_start, gs, gl, scale, inp.k_self.f64,
+                                inp.v_self.f64)
+    for name, want in zip(("dq", "dk", "dv", "dks", "dvs"), r):
+        got = np.fromfile(d / f"{name}.bin", np.float32).astype(np.float64).reshape(want.shape)
+        assert rel_frob(got, want) <= 3e-2, name
