@@ -102,3 +102,30 @@ def test_lpt_matches_oracle_bit_exact(lib, n_bin, per_bin, pool, wide):
     bins, load = sxattn.lpt_assign(cost, n_bin)
     assert bins.tolist() == want_bins
     assert load.tolist() == want_load
+
+
+def test_workspace_size_queries(lib):
+    """Sizes of the optional workspaces: 0 for invalid sizes; the split schedule's
+    scratch holds the job list, the split-group list and float32 slots for at most
+    2 n_cu / hkv pieces of 256 rows (n_cu: the device's compute units, 256 where no
+    device answers); the backward's split size is its plain size rounded up to 256
+    plus the same scratch."""
+    import torch
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    up = lambda x: -(-x // 256) * 256
+    assert lib.sparse_xattn_fwd_split_workspace_bytes(512, 32, 8, 96) == 0
+    assert lib.sparse_xattn_fwd_split_workspace_bytes(512, 30, 8, 128) == 0
+    assert lib.sparse_xattn_fwd_split_workspace_bytes(-1, 32, 8, 128) == 0
+    assert lib.sparse_xattn_fwd_split_workspace_bytes(0, 32, 8, 128) == 0        # no row group
+    assert lib.sparse_xattn_fwd_split_workspace_bytes(4096 * 4 + 1, 32, 8, 128) == 0  # > 4096 groups
+    assert lib.sparse_xattn_bwd_split_workspace_bytes(512, 65536, 32, 8, 96) == 0
+    for n_blk, hq, hkv, d in ((512, 32, 8, 128), (40, 40, 1, 64), (3, 12, 4, 128)):
+        split = lib.sparse_xattn_fwd_split_workspace_bytes(n_blk, hq, hkv, d)
+        groups = -(-n_blk * 16 * (hq // hkv) // 256)
+        assert lib.sparse_xattn_fwd_workspace_bytes(n_blk, hq, hkv) == 4 * groups
+        pieces = max(2, -(-2 * n_cu // hkv))
+        assert split == (up(16 * (groups + pieces)) + up(16 * (pieces // 2))
+                         + up(4 * pieces * hkv * 256) + 4 * pieces * hkv * 256 * d)
+        n_loc = 8192
+        bwd = lib.sparse_xattn_bwd_workspace_bytes(n_blk, n_loc, hq, hkv, d)
+        assert lib.sparse_xattn_bwd_split_workspace_bytes(n_blk, n_loc, hq, hkv, d) == up(bwd) + split
