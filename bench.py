@@ -55,7 +55,7 @@ if ROOT not in sys.path:
 METRIC = "useful attn TFLOP/s fwd+bwd, 8k q × 64k ctx bf16; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-WORKLOAD = "fwd_bf16_8kq_64k"
+WORKLOAD = "fwdbwd_bf16_8kq_64k"
 
 
 def log(*a):
@@ -111,16 +111,22 @@ class Timers:
         return agg
 
 
-def build_problem(torch, seed, split=False):
+def build_problem(torch, seed, split=False, inputs=None):
+    """Device buffers, plan buffers, streams and events of the benchmark step.
+    ``inputs`` (a function of the workload and its metadata returning synth.Inputs
+    over the whole context) replaces the default draw, for tests that run the step on
+    other values."""
     from block_sparse_cross_anchor_amd import synth, sxattn
 
     w = synth.WORKLOADS[WORKLOAD]
     meta = synth.meta_for(w, seed)
     all_rows = np.arange(w.n_ctx)
-    std = w.std()
-    inp = synth.draw_inputs(seed, meta, w.hq, w.hkv, w.d, "bf16", std,
-                            np.array([0], np.int32), np.array([w.n_ctx], np.int32),
-                            with_dout=True)
+    if inputs is None:
+        inp = synth.draw_inputs(seed, meta, w.hq, w.hkv, w.d, "bf16", w.std(),
+                                np.array([0], np.int32), np.array([w.n_ctx], np.int32),
+                                with_dout=True)
+    else:
+        inp = inputs(w, meta)
 
     def dev(t):
         return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(
@@ -174,6 +180,7 @@ def build_problem(torch, seed, split=False):
         m.chunk_gstart, m.chunk_len = P["plan_gs"][b], P["plan_gl"][b]
         m.n_blk, m.n_chunk, m.n_loc = w.n_anchor, per_bin, n_loc
         P["metas"].append(m)
+    P["live_rows"] = {}   # live partial rows of the combine, per plan
     P["ev_fork"] = torch.cuda.Event()
     P["ev_cost"] = torch.cuda.Event()
     P["ev_fork_dq"] = torch.cuda.Event()
@@ -257,7 +264,22 @@ def step(torch, P, T):
     T.run("gather_fwd", 4.0 * d * hq * fwd_pairs, gathers_and_forwards, launches=nb)
     bin_pairs = [int(cost_np[order[b]].sum()) for b in range(nb)]   # after the launches
     rows = w.n_q * hq
-    T.run("lse_combine", nb * rows * (d * 2 + 4) + rows * (d * 2 + 4),
+    # the combine's algorithmic bytes: O rows of the live partials only (a partial row
+    # is empty where the block's interval meets none of the bin's chunks, and the
+    # kernel does not read it), every lse, and the merged output
+    key = bins_np.tobytes()
+    if key not in P["live_rows"]:
+        meta = P["meta"]
+        lo = meta.sample_start.astype(np.int64)[:, None]
+        hi = meta.anchor.astype(np.int64)[:, None]
+        cs = P["chunk_gs"].astype(np.int64)[order]                   # [nb, per_bin]
+        ce = cs + P["chunk_gl"].astype(np.int64)[order]
+        live = [np.any(np.maximum(lo, cs[b][None, :]) < np.minimum(hi, ce[b][None, :]), axis=1)
+                for b in range(nb)]
+        live[0][:] = True   # bin 0 carries the own-block term
+        P["live_rows"][key] = int(sum(int(x.sum()) for x in live)) * 16 * hq
+    live_rows = P["live_rows"][key]
+    T.run("lse_combine", live_rows * d * 2 + nb * rows * 4 + rows * (d * 2 + 4),
           lambda: sxattn.lse_combine(P["o_parts"].view(nb, rows, d), P["lse_parts"].view(nb, rows),
                                      out=P["o"], lse_out=P["lse"]))
     o = P["o"].view(w.n_q, hq, d)
@@ -669,9 +691,9 @@ def combine_study(torch, n_parts, seed, reps):
     the empty pattern of the 524288-token workload planned onto n_parts bins (a
     partial is empty, lse = -inf, where the block's interval meets none of that bin's
     chunks; the kernel never reads such a partial's O).  Eight seeded partial sets are
-    drawn and repeated across the n_parts slots.  Prints one JSON line with each
-    case's time per call and its rate in algorithmic bytes (O rows of live partials,
-    every lse, the output)."""
+    drawn and repeated across the n_parts slots.  Returns each case's time per call
+    and its rate in algorithmic bytes (O rows of live partials, every lse, the
+    output)."""
     from block_sparse_cross_anchor_amd import synth, sxattn
 
     w = synth.WORKLOADS["cp64_share_8kq_512k"]
@@ -723,7 +745,9 @@ def combine_study(torch, n_parts, seed, reps):
         result[name] = {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
                         "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
                         "live_fraction": round(live_rows / (n_parts * rows), 4)}
-    print(json.dumps(result), flush=True)
+    del o_parts, lse_dense, lse_empty, out_o, out_l
+    torch.cuda.empty_cache()
+    return result
 
 
 def main():
@@ -738,7 +762,7 @@ def main():
                     help="run the step's forwards and dQ phases on the split schedule")
     ap.add_argument("--balance", metavar="WORKLOAD",
                     help="instead of the benchmark, the per-bin balance study of a workload "
-                         "with bins (fwd_bf16_8kq_64k or cp64_share_8kq_512k)")
+                         "with bins (fwdbwd_bf16_8kq_64k or cp64_share_8kq_512k)")
     ap.add_argument("--reps", type=int, default=5,
                     help="launches per timed share (--balance) or phase (--dense)")
     ap.add_argument("--combine", type=int, metavar="P",
@@ -770,7 +794,8 @@ def main():
         dense_study(torch, args.dense, args.seed, max(args.reps, 1))
         return
     if args.combine:
-        combine_study(torch, args.combine, args.seed, max(args.reps, 1))
+        print(json.dumps(combine_study(torch, args.combine, args.seed, max(args.reps, 1))),
+              flush=True)
         return
     log("building the synthetic workload ...")
     P = build_problem(torch, args.seed, split=args.split)
@@ -847,6 +872,16 @@ def main():
                         "rate the forward's FLOP over that span; bwd_dq runs two halves of the "
                         "query blocks on two streams",
     }
+    # the combine one device performs at context-parallel size 64 (the 8192-query view,
+    # 64 bf16 partials), every partial live and with the real empty pattern
+    log("timing the 64-way combine of the 8192-query view ...")
+    comb = combine_study(torch, 64, 5, 10)
+    out["combine_64way"] = {
+        "all_live": comb["all_live"], "empty_pattern": comb["empty_pattern"],
+        "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "note": "lse_combine of 64 bf16 partials of all 262144 query rows (d 128), HIP events "
+                "around 10 back-to-back calls; bytes are the O rows of live partials, every "
+                "lse and the merged output"}
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s ...")
         out["cpu_baseline"] = cpu_baseline(P, args.cpu_seconds)

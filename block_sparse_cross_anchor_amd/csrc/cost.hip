@@ -1,8 +1,9 @@
 // Realised attention cost per contiguous context chunk.
 //
-// Split-KV costs every context chunk from its actual attention usage, which the
-// global query view makes computable locally ("Split-KV speeds diffusion drafter
-// training...", section "Balance actual attention work").  Block b's B query
+// Split-KV prices each context chunk by the attention work that lands on it; every
+// device holds all query blocks' metadata, so each can count it for every chunk
+// ("Split-KV speeds diffusion drafter training...", section "Balance actual
+// attention work").  Block b's B query
 // tokens may read keys [sample_start[b], anchor[b]); the cost of chunk c is the
 // number of such (query token, key) pairs with the key inside the chunk, i.e.
 // B * sum_b |[sample_start[b], anchor[b]) intersect chunk c|, computed exactly in

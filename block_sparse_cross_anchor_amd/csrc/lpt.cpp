@@ -1,7 +1,7 @@
 // Longest-processing-time-first assignment of context chunks to devices with equal
 // chunk counts ("Split-KV speeds diffusion drafter training...", section "Balance
-// actual attention work": chunks sorted by cost, each expensive chunk given to the
-// least-loaded eligible device, chunk counts kept equal).
+// actual attention work": costly chunks first, each to the device with the least
+// work among those with room left, every device ending with the same count).
 //
 // Chunks are visited by (cost descending, index ascending).  A min-heap keyed by
 // (load, bin index) holds the bins that still have room; the chosen bin is popped,

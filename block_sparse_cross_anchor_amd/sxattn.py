@@ -172,18 +172,22 @@ _workspaces = {}
 
 
 def _scratch(kind: str, need: int, device) -> torch.Tensor:
-    """Cached device scratch per (kind, device), grown on demand.  Calls that share
-    it must be ordered on one stream."""
-    key = (kind, torch.device(device))
+    """Cached device scratch per (kind, device, current stream), grown on demand.  Calls
+    on one stream share it and are ordered by that stream; calls on different streams
+    get different buffers, so they never race on it."""
+    dev = torch.device(device)
+    key = (kind, dev, torch.cuda.current_stream(dev).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=key[1])
+        # allocated on this stream: torch reuses a replaced buffer only in this
+        # stream's order, after the work queued on it
+        ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
 
 def bwd_workspace(n_blk: int, n_loc: int, hq: int, hkv: int, d: int, device, split=False):
-    """Scratch of the load-balanced dQ and dK/dV phases (cached per device), with the
+    """Scratch of the load-balanced dQ and dK/dV phases (cached per device and stream), with the
     split dQ schedule's plan and slots when ``split``.  Returns (tensor, bytes to pass)."""
     lib = load_library()
     size = lib.sparse_xattn_bwd_split_workspace_bytes if split else lib.sparse_xattn_bwd_workspace_bytes

@@ -60,13 +60,17 @@ class Workload:
         return 1.0 if self.value_std == "unit" else 1.0 / np.sqrt(d)
 
 
-# The five workloads (tiny fp32 -> one device's share at CP size 64).
+# The five workloads (tiny fp32 -> one device's share at CP size 64), plus the
+# benchmark's forward+backward step on the 8192-query x 65536-token shapes.
 WORKLOADS = {
     "tiny_fp32_512": Workload("tiny_fp32_512", 512, 512, 512, 4, 2, 2, 64, "f32", "unit", 256),
     "fwd_bf16_512q_4k": Workload("fwd_bf16_512q_4k", 4096, 512, 2048, 32, 32, 8, 128, "bf16",
                                  "inv_sqrt_d", 1024),
     "fwd_bf16_8kq_64k": Workload("fwd_bf16_8kq_64k", 65536, 4096, 32768, 512, 32, 8, 128, "bf16",
                                  "inv_sqrt_d", 1024, n_bin=8),
+    # the same shapes and draws, forward and backward: the benchmark's step
+    "fwdbwd_bf16_8kq_64k": Workload("fwdbwd_bf16_8kq_64k", 65536, 4096, 32768, 512, 32, 8, 128,
+                                    "bf16", "inv_sqrt_d", 1024, n_bin=8, bwd=True),
     "fwdbwd_bf16_4kq_32k": Workload("fwdbwd_bf16_4kq_32k", 32768, 4096, 32768, 256, 32, 8, 128,
                                     "bf16", "inv_sqrt_d", 4096, bwd=True),
     "cp64_share_8kq_512k": Workload("cp64_share_8kq_512k", 524288, 8192, 65536, 512, 32, 8, 128,

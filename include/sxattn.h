@@ -191,8 +191,8 @@ int lse_combine(const void* o_parts, sxa_dtype part_dtype, const float* lse_part
 
 /*
  * Realised attention cost of every contiguous context chunk
- * ("Balance actual attention work": each chunk is costed from its actual
- * attention usage, computable from the global query view).
+ * ("Balance actual attention work": a chunk is priced by the attention work that
+ * lands on it, which any device can count from the metadata of all query blocks).
  *   cost_out[c] (device int64, c < ceil(n_ctx / chunk_size)) = number of
  *   (query token, key) pairs with the key in [c*chunk_size, min((c+1)*chunk_size, n_ctx))
  *   allowed by the anchor mask, for one head; own-block pairs are not counted.

@@ -8,11 +8,12 @@ queries change the problem": each draft block opened by an anchor attends to
 the preceding context of its own sample and to every token of its own block.
 Readings taken where the page is silent (all listed in the design notes):
 
-* "preceding context within its own sample" = global packed positions j with
-  sample_start[b] <= j < anchor[b]; the anchor position itself is excluded;
-* "all tokens inside that block" = the block's own draft tokens, whose keys and
-  values are supplied separately (``k_self``/``v_self``, rows b*B..b*B+B-1),
-  attended bidirectionally;
+* the context a block reads = global packed positions j with
+  sample_start[b] <= j < anchor[b] (same sample, strictly before the anchor;
+  the anchor position itself is excluded);
+* the block's own tokens = its draft tokens, whose keys and values are supplied
+  separately (``k_self``/``v_self``, rows b*B..b*B+B-1), attended
+  bidirectionally (all of them, no causal order);
 * grouped-query heads: query head h reads kv head h // (hq // hkv);
 * logits are ``scale * <q, k>`` with ``scale`` taken as a float32 value; the
   log-sum-exp is natural-log and includes the scale; a row with no allowed key

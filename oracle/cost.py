@@ -2,10 +2,10 @@
 
 Test infrastructure only; never used by the product path.
 
-Split-KV gives each context chunk a cost based on its actual attention usage,
-which the global query view makes computable on every device ("Split-KV speeds
-diffusion drafter training...", section "Balance actual attention work").
-Reading taken here: the cost of a chunk is the number of (query token, context
+The planner prices each context chunk by the attention work that lands on it;
+since every device holds the metadata of all query blocks, each device can count
+that work for every chunk ("Split-KV speeds diffusion drafter training...",
+section "Balance actual attention work").  Reading taken here: the cost of a chunk is the number of (query token, context
 key) pairs inside the chunk that the anchor mask allows, for one head (all
 heads cost the same); own-block pairs are not context work and are not
 counted.  Chunks are the contiguous fixed-size spans

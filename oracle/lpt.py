@@ -2,9 +2,9 @@
 
 Test infrastructure only; never used by the product path.
 
-Split-KV's planner sorts context chunks by cost and gives each expensive chunk
-to the least-loaded eligible device while keeping the number of chunks per
-device equal ("Split-KV speeds diffusion drafter training...", section
+Split-KV's planner visits context chunks from the most to the least costly and
+puts each on the device with the least work so far among those that still have
+room, so that every device ends with the same number of chunks ("Split-KV speeds diffusion drafter training...", section
 "Balance actual attention work").  Readings taken where the page is silent:
 
 * eligible = holding fewer than n_chunk / n_bin chunks (n_chunk must be a

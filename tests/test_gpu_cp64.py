@@ -10,7 +10,11 @@ chunks are the local shard.  On it:
     (block, bin) pattern is the real one (a partial is empty where the block's
     interval meets none of that bin's chunks);
   * the backward of the shard from the combined O and lse: dQ and the own-block
-    dK, dV of sampled blocks, and dK, dV of 64-key windows of the shard.
+    dK, dV of sampled blocks, and dK, dV of 64-key windows of the shard: lightly read
+    ones and the most heavily read ones (whose tiles the dK/dV schedule splits
+    across workgroups).
+A second test runs the mask-boundary probe (Q = 0, one-hot values; tests/probe.py)
+on the shard and checks every output against its closed form.
 The split schedule (forward and dQ) is compared with the default schedule on the
 whole share.  The combine and the backward take the combined values only for the
 blocks that are checked (sampled blocks and the readers of the windows; rows are independent),
@@ -26,9 +30,11 @@ import pytest
 import torch
 
 import oracle
+import probe
 from block_sparse_cross_anchor_amd import synth, sxattn
-from helpers import (assert_lse_close, dev, device_meta, head_rows, host64, pick_windows,
-                     rel_frob, sub_blocks, token_rows)
+from helpers import (assert_lse_close, dev, device_meta, dkdv_split_tiles, head_rows,
+                     heavy_windows, host64, pick_windows, rel_frob, share_pairs, sub_blocks,
+                     token_rows)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -74,6 +80,14 @@ def test_cp64_bin0_share_forward_combine_backward_sampled():
                                         rng.integers(0, meta.n_blk, 2)]))
     windows = pick_windows(meta, gs, gl, rng, 3, 24)
     assert len(windows) == 3
+    # and the most heavily read windows of the shard, whose tiles the dK/dV schedule
+    # splits across workgroups and adds up in its fix-up pass
+    heavy = heavy_windows(meta, gs, gl, 3, 2e7, pairs_of=lambda r: share_pairs(meta, r, gs, gl))
+    assert len(heavy) >= 3 and heavy[0][2].size > 24
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    shares = dkdv_split_tiles(meta, gs, gl, hq, hkv, n_cu, True)
+    assert sum(int(shares[l0 // 256] >= 2) for l0, _, _ in heavy) >= 1
+    windows += heavy
     need = np.unique(np.concatenate([sampled] + [r for _, _, r in windows]))
     sub = sub_blocks(meta, need)
     trows = token_rows(need)
@@ -143,3 +157,49 @@ def test_cp64_bin0_share_forward_combine_backward_sampled():
         assert np.abs(rr[1]).max() > 0
         assert rel_frob(host64(dk)[l0:l0 + 64], rr[1]) <= 3e-2, (l0, g0)
         assert rel_frob(host64(dv)[l0:l0 + 64], rr[2]) <= 3e-2, (l0, g0)
+
+
+def test_cp64_bin0_share_boundary_probe_all_outputs():
+    """Q = 0 with one-hot probe values on bin 0's shard (own-block term included),
+    forward then backward from the shard's own O and lse: O and lse of all 262144 query
+    rows, dV of all 8192 local keys (per 256-key tile), dK = 0, and dQ of every row,
+    against the closed forms of tests/probe.py (pinned against the oracle on the CPU)."""
+    w = synth.WORKLOADS["cp64_share_8kq_512k"]
+    seed = 5
+    n_q, hq, hkv, d, nb = w.n_q, w.hq, w.hkv, w.d, w.n_bin
+    scale = 1.0 / math.sqrt(d)
+    meta = synth.meta_for(w, seed)
+    anchor = torch.as_tensor(meta.anchor).cuda()
+    start = torch.as_tensor(meta.sample_start).cuda()
+    cost = sxattn.chunk_cost(anchor, start, w.n_ctx, w.chunk_size).cpu()
+    bins = sxattn.lpt_assign(cost, nb)[0].numpy()
+    gs_all, gl_all = synth.contiguous_chunks(w.n_ctx, w.chunk_size)
+    mine = np.flatnonzero(bins == 0)
+    gs, gl = gs_all[mine], gl_all[mine]
+    inp = probe.inputs(seed, meta, hq, hkv, d, gs, gl, w.chunk_size)
+    q, k, v, ks, vs, do = (dev(t) for t in (inp.q, inp.k, inp.v, inp.k_self, inp.v_self, inp.dout))
+    dm = device_meta(meta, gs, gl)
+    o, lse = sxattn.sparse_xattn_fwd(q, k, v, dm, scale, ks, vs)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+    dk, dv, dks, dvs = sxattn.sparse_xattn_bwd(q, k, v, dm, scale, o, do, lse, dq, ks, vs)
+    torch.cuda.synchronize()
+    n_b, hits = probe.forward(meta, gs, gl, w.chunk_size, seed)
+    want = np.repeat(hits / n_b[:, None], 16, axis=0)[:, None, :]
+    og = host64(o)
+    err = np.abs(og[..., :probe.N_COLS] - want)
+    assert np.all(err <= 2 ** -8 * want + 1e-6), float(err.max())
+    assert np.all(og[..., probe.N_COLS:] == 0)
+    np.testing.assert_allclose(host64(lse), np.repeat(np.log(n_b), 16)[:, None] * np.ones((1, hq)),
+                               rtol=0, atol=1e-5)
+    want_v = probe.dv_context(meta, inp, gs, gl, hq, hkv)
+    got_v = host64(dv)
+    for t0 in range(0, want_v.shape[0], 256):
+        assert rel_frob(got_v[t0:t0 + 256], want_v[t0:t0 + 256]) <= 1e-2, t0
+    assert torch.count_nonzero(dk).item() == 0 and torch.count_nonzero(dks).item() == 0
+    assert rel_frob(host64(dvs), probe.dv_self(meta, inp, gs, gl, hq, hkv)) <= 1e-2
+    want_q = probe.dq(meta, inp, gs, gl, hq, hkv, scale, w.chunk_size, seed)
+    got_q = host64(dq)
+    assert rel_frob(got_q, want_q) <= 1e-2
+    for b in range(meta.n_blk):
+        r = slice(16 * b, 16 * b + 16)
+        assert rel_frob(got_q[r], want_q[r]) <= 3e-2, b

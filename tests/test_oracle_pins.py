@@ -414,6 +414,21 @@ def test_lpt_golden():
         assert b == case["bin_of_chunk"] and load == case["bin_load"]
 
 
+def test_imbalance_golden():
+    """The work imbalance of a plan against hand-worked exact fractions (max / mean - 1).
+    The values separate it from the plausible wrong readings: max / min - 1 gives 1/16
+    on [17, 16] and is undefined on [8, 3, 3, 0]; (max - mean) / max gives 1/34."""
+    from fractions import Fraction
+
+    g = json.load(open(os.path.join(GOLDEN, "lpt_tiny.json")))
+    cases = [(c["bin_load"], c["imbalance"]) for c in g["cases"]]
+    cases += [(c["load"], c["imbalance"]) for c in g["imbalance_extra"]]
+    assert len(cases) >= 7
+    for load, want in cases:
+        got = oracle.imbalance(load)
+        assert abs(got - float(Fraction(want))) <= 1e-15, (load, got, want)
+
+
 @pytest.mark.parametrize("seed", range(10))
 def test_lpt_properties(seed):
     rng = np.random.default_rng(seed)
