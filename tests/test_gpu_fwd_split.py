@@ -51,7 +51,8 @@ def group_tiles(meta, hq, hkv, gs, gl, with_self):
 def read_plan(n_groups, hkv):
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     pieces = max(2, -(-2 * n_cu // hkv))
-    ws = sxattn._workspaces[("fwd_split", torch.device("cuda", torch.cuda.current_device()))]
+    ws = sxattn._workspaces[("fwd_split", torch.device("cuda", torch.cuda.current_device()),
+                             torch.cuda.current_stream().cuda_stream)]
     jobs = ws[:16 * (n_groups + pieces)].cpu().numpy().view(np.int32).reshape(-1, 4)
     return jobs, pieces
 
@@ -223,7 +224,8 @@ def test_split_dq_matches_unsplit_and_oracle(case):
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     pieces = max(2, -(-2 * n_cu // hkv))
     tiles = group_tiles(meta, hq, hkv, gs, gl, with_self)
-    ws = sxattn._workspaces[("bwd_split", torch.device("cuda", torch.cuda.current_device()))]
+    ws = sxattn._workspaces[("bwd_split", torch.device("cuda", torch.cuda.current_device()),
+                             torch.cuda.current_stream().cuda_stream)]
     jobs = ws[base:base + 16 * (len(tiles) + pieces)].cpu().numpy().view(np.int32).reshape(-1, 4)
     assert check_plan(jobs, pieces, tiles) > 0
     dq_u = host64(out["auto", "over"])
