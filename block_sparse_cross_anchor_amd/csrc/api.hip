@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 
@@ -89,6 +90,37 @@ int check_attn(const void* q, const void* k, const void* v, sxa_dtype in_dtype, 
   return SXA_OK;
 }
 
+// Scratch of sparse_xattn_fwd_noalloc: the forward's ranked dispatch order (one int32
+// per query row group of 256 rows, up to kMaxOrderedGroups) in a file-scope device
+// array, so that the call allocates nothing.  Every device that runs the library holds
+// its own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address is looked up once per device
+// with hipGetSymbolAddress and only that address is passed to kernels.
+constexpr int kNoallocScratchInts = sxa::kMaxOrderedGroups;
+static __device__ __align__(256) int32_t scratch[kNoallocScratchInts];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// Device address of `scratch` on the current device (looked up on its first use there).
+int scratch_on_current_device(int32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SXA_EUNSUPPORTED, "device index %d is beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(SXA_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<int32_t*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return SXA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,6 +162,42 @@ int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_d
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(in_dtype == SXA_BF16 ? sxa::launch_fwd_bf16(a, s) : sxa::launch_fwd_f32(a, s),
                     "sparse_xattn_fwd launch");
+}
+
+int sparse_xattn_fwd_noalloc(const void* q, const void* k, const void* v, sxa_dtype in_dtype,
+                             int32_t n_blk, int32_t block_size, int32_t hq, int32_t hkv, int32_t d,
+                             float scale, const int32_t* anchor, const int32_t* sample_start,
+                             const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
+                             int64_t n_loc, const void* k_self, const void* v_self, void* o,
+                             sxa_dtype o_dtype, float* lse, void* stream) {
+  sxa::AttnArgs a;
+  int st = check_attn(q, k, v, in_dtype, n_blk, block_size, hq, hkv, d, scale, anchor,
+                      sample_start, chunk_gstart, chunk_len, n_chunk, n_loc, k_self, v_self, a);
+  if (st != SXA_OK) return st;
+  if (!dtype_ok(o_dtype)) return fail(SXA_EINVAL, "o_dtype %d is not a valid sxa_dtype", o_dtype);
+  if (in_dtype == SXA_F32 && o_dtype != SXA_F32)
+    return fail(SXA_EUNSUPPORTED, "float32 inputs need a float32 output");
+  if (n_blk > 0 && (o == nullptr || lse == nullptr)) return fail(SXA_EINVAL, "o and lse must not be NULL");
+  const int64_t groups = sxa::row_groups(a, sxa::kRowsPerGroup);
+  if (groups > kNoallocScratchInts)
+    return fail(SXA_EUNSUPPORTED,
+                "sparse_xattn_fwd_noalloc: %lld query row groups of 256 rows per kv head exceed the "
+                "static scratch of %d (use sparse_xattn_fwd with a workspace)",
+                static_cast<long long>(groups), kNoallocScratchInts);
+  a.o = o;
+  a.o_bf16 = o_dtype == SXA_BF16;
+  a.lse = lse;
+  a.row_split = nullptr;
+  a.n_cu = 0;
+  if (n_blk == 0) return ok();
+  if (in_dtype == SXA_BF16) {
+    int32_t* order = nullptr;
+    if ((st = scratch_on_current_device(&order)) != SXA_OK) return st;
+    a.rg_order = order;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(in_dtype == SXA_BF16 ? sxa::launch_fwd_bf16(a, s) : sxa::launch_fwd_f32(a, s),
+                    "sparse_xattn_fwd_noalloc launch");
 }
 
 int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_dtype,

@@ -22,7 +22,7 @@ SXA_OK, SXA_EINVAL, SXA_EUNSUPPORTED, SXA_EHIP = 0, -1, -2, -3
 BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_DQ_OVERWRITE = 1, 2, 4, 8
 BLOCK = 16
 
-EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_fwd_workspace_bytes",
+EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_fwd_noalloc", "sparse_xattn_fwd_workspace_bytes",
            "sparse_xattn_fwd_split_workspace_bytes", "sparse_xattn_bwd",
            "sparse_xattn_bwd_workspace_bytes", "sparse_xattn_bwd_split_workspace_bytes",
            "lse_combine", "chunk_cost", "lpt_assign", "context_gather", "sxa_last_error")
@@ -51,6 +51,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     attn_common = [P, P, P, ctypes.c_int, I32, I32, I32, I32, I32, F32, P, P, P, P, I32, I64, P, P]
     lib.sparse_xattn_fwd.argtypes = attn_common + [P, ctypes.c_int, P, P, I64, P]
     lib.sparse_xattn_fwd.restype = ctypes.c_int
+    lib.sparse_xattn_fwd_noalloc.argtypes = attn_common + [P, ctypes.c_int, P, P]
+    lib.sparse_xattn_fwd_noalloc.restype = ctypes.c_int
     lib.sparse_xattn_fwd_workspace_bytes.argtypes = [I32, I32, I32]
     lib.sparse_xattn_fwd_workspace_bytes.restype = I64
     lib.sparse_xattn_fwd_split_workspace_bytes.argtypes = [I32, I32, I32, I32]
@@ -165,6 +167,33 @@ def sparse_xattn_fwd(q, k, v, meta: Meta, scale: float, k_self=None, v_self=None
         _ptr(meta.anchor), _ptr(meta.sample_start), _ptr(meta.chunk_gstart), _ptr(meta.chunk_len),
         meta.n_chunk, meta.n_loc, _ptr(k_self), _ptr(v_self), _ptr(out), _dtype_code(out),
         _ptr(lse), _ptr(workspace), ws_bytes, _stream()))
+    return out, lse
+
+
+def sparse_xattn_fwd_noalloc(q, k, v, meta: Meta, scale: float, k_self=None, v_self=None,
+                             out=None, lse=None):
+    """sparse_xattn_fwd through the entry point that allocates nothing (its row-group
+    ranking lives in a static device array of the library).  ``out`` and ``lse`` are
+    required, so that the call itself allocates nothing either.  Returns (o, lse)."""
+    n_q, hq, d = q.shape
+    hkv = k.shape[1]
+    _need(q, "q", dtype=q.dtype)
+    _need(k, "k", (meta.n_loc, hkv, d), q.dtype)
+    _need(v, "v", (meta.n_loc, hkv, d), q.dtype)
+    if k_self is not None:
+        _need(k_self, "k_self", (n_q, hkv, d), q.dtype)
+        _need(v_self, "v_self", (n_q, hkv, d), q.dtype)
+    if n_q != meta.n_blk * BLOCK:
+        raise ValueError("q rows must equal 16 * number of blocks")
+    if out is None or lse is None:
+        raise ValueError("sparse_xattn_fwd_noalloc needs caller-allocated out and lse")
+    _need(out, "out", (n_q, hq, d))
+    _need(lse, "lse", (n_q, hq), torch.float32)
+    _check(load_library().sparse_xattn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), meta.n_blk, BLOCK, hq, hkv, d, float(scale),
+        _ptr(meta.anchor), _ptr(meta.sample_start), _ptr(meta.chunk_gstart), _ptr(meta.chunk_len),
+        meta.n_chunk, meta.n_loc, _ptr(k_self), _ptr(v_self), _ptr(out), _dtype_code(out),
+        _ptr(lse), _stream()))
     return out, lse
 
 

@@ -103,6 +103,29 @@ int sparse_xattn_fwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                      void* o, sxa_dtype o_dtype, float* lse, void* workspace,
                      int64_t workspace_bytes, void* stream);
 
+/*
+ * sparse_xattn_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, results and errors are those of sparse_xattn_fwd
+ * called with a workspace of sparse_xattn_fwd_workspace_bytes() bytes: the bf16 path
+ * ranks its query row groups and dispatches the heaviest first (no split schedule),
+ * with the ranking kept in a library-owned static device array of 4096 int32 (16 KiB)
+ * that every device running the library holds until the process ends.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine); the caller still
+ * passes inputs and outputs.  Beyond 4096 row groups of 256 query rows per kv head
+ * (n_blk * 16 * hq / hkv > 1048576) it returns SXA_EUNSUPPORTED before anything is
+ * enqueued.  Every call on one device uses that device's array, which keeps the last
+ * call's contents (nothing in it needs clearing: each call rewrites what it reads);
+ * calls that overlap on one device (concurrent streams or threads) race on it and
+ * must be ordered by the caller.
+ */
+int sparse_xattn_fwd_noalloc(const void* q, const void* k, const void* v, sxa_dtype in_dtype,
+                             int32_t n_blk, int32_t block_size, int32_t hq, int32_t hkv, int32_t d,
+                             float scale, const int32_t* anchor, const int32_t* sample_start,
+                             const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
+                             int64_t n_loc, const void* k_self, const void* v_self, void* o,
+                             sxa_dtype o_dtype, float* lse, void* stream);
+
 /* Workspace bytes of sparse_xattn_fwd's load balancing (0 for invalid sizes). */
 int64_t sparse_xattn_fwd_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv);
 
