@@ -11,8 +11,8 @@ tokens and planned onto 8 virtual devices ("bins"):
      sparse_xattn_fwd (the own-block term on bin 0): partial O, lse; the bins
      alternate between two streams, so their gathers and forwards overlap
   4. lse_combine  of the 8 partials
-  5. sparse_xattn_bwd: delta pre-pass, then the dQ phase of every bin (accumulated)
-     and the dK/dV phase of every bin
+  5. sparse_xattn_bwd: delta pre-pass, then the dQ phase of every bin (accumulated,
+     on a second stream) beside the dK/dV phase of every bin (bf16 dK, dV)
 
 Throughput is useful attention FLOP/s: 4*d*Hq FLOP per allowed (query, key) pair
 for the forward and 10*d*Hq for the backward, over the allowed pairs only
@@ -111,7 +111,7 @@ class Timers:
         return agg
 
 
-def build_problem(torch, seed, split=False, inputs=None):
+def build_problem(torch, seed, split=False, inputs=None, bwd_schedule="overlap"):
     """Device buffers, plan buffers, streams and events of the benchmark step.
     ``inputs`` (a function of the workload and its metadata returning synth.Inputs
     over the whole context) replaces the default draw, for tests that run the step on
@@ -147,9 +147,10 @@ def build_problem(torch, seed, split=False, inputs=None):
     bf, f32 = torch.bfloat16, torch.float32
     P["k_loc"] = torch.empty((nb, n_loc, hkv, d), dtype=bf, device="cuda")
     P["v_loc"] = torch.empty_like(P["k_loc"])
-    P["dk_loc"] = torch.empty((nb, n_loc, hkv, d), dtype=f32, device="cuda")
+    # key/value gradients in bf16 (summed in float32 inside the library, rounded once)
+    P["dk_loc"] = torch.empty((nb, n_loc, hkv, d), dtype=bf, device="cuda")
     P["dv_loc"] = torch.empty_like(P["dk_loc"])
-    P["dks"] = torch.empty(P["ks"].shape, dtype=f32, device="cuda")
+    P["dks"] = torch.empty(P["ks"].shape, dtype=bf, device="cuda")
     P["dvs"] = torch.empty_like(P["dks"])
     P["o_parts"] = torch.empty((nb, n_q, hq, d), dtype=bf, device="cuda")
     P["lse_parts"] = torch.empty((nb, n_q, hq), dtype=f32, device="cuda")
@@ -172,6 +173,7 @@ def build_problem(torch, seed, split=False, inputs=None):
     # workspace; the two events that fork and join the streams are created here,
     # outside any timed region.
     P["side_stream"] = torch.cuda.Stream()
+    P["bwd_schedule"] = bwd_schedule
     # each bin's call metadata: views of the device plan, which every step rewrites
     P["metas"] = []
     for b in range(nb):
@@ -291,15 +293,22 @@ def step(torch, P, T):
         return (P["q"][t], P["k_loc"][b], P["v_loc"][b], hf["metas"][b], scale, o[t], P["do"][t],
                 lse[t], P["dq"][t])
 
-    def deltas():   # the whole rows (for dK/dV), then each dQ half's own
+    def whole_delta():
         sxattn.sparse_xattn_bwd(P["q"], P["k_loc"][0], P["v_loc"][0], metas[0], scale, o, P["do"],
                                 lse, P["dq"], delta_ws=P["delta"], dk=P["dk_loc"][0],
                                 dv=P["dv_loc"][0], flags=sxattn.BWD_DELTA)
+
+    def deltas():   # the whole rows (for dK/dV), then each dQ half's own
+        whole_delta()
         for hf in halves:
             sxattn.sparse_xattn_bwd(*half_args(hf, 0), delta_ws=hf["delta"], dk=P["dk_loc"][0],
                                     dv=P["dv_loc"][0], flags=sxattn.BWD_DELTA, workspace=hf["ws"])
 
-    T.run("delta", 2 * rows * (2 * d * 2 + 4), deltas, launches=3)
+    sched = P["bwd_schedule"]
+    if sched == "halves":
+        T.run("delta", 2 * rows * (2 * d * 2 + 4), deltas, launches=3)
+    else:
+        T.run("delta", rows * (2 * d * 2 + 4 + 8), whole_delta, launches=1)
     all_pairs = sum(bin_pairs) + self_pairs
 
     def dq_halves():
@@ -325,11 +334,31 @@ def step(torch, P, T):
             self_kv[0], self_kv[1], delta_ws=P["delta"], dk=P["dk_loc"][b], dv=P["dv_loc"][b],
             dk_self=P["dks"], dv_self=P["dvs"], flags=flags)
 
-    # dQ: both halves' bins on two streams (bin 0 overwrites a half's rows, the others
-    # add); dK/dV: one group of nb launches on this stream
-    T.run("bwd_dq", 6.0 * d * hq * all_pairs, dq_halves, launches=2 * nb)
-    T.run("bwd_dkdv", 8.0 * d * hq * all_pairs,
-          lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)], launches=nb)
+    def dq_bins():
+        for b in range(nb):
+            bwd(b, sxattn.BWD_DQ | (sxattn.BWD_DQ_OVERWRITE if b == 0 else 0))
+
+    dq_work, dkdv_work = 6.0 * d * hq * all_pairs, 8.0 * d * hq * all_pairs
+    # the dK/dV phase alone (same inputs and plan), for its roofline outside the step
+    P["dkdv_phase"] = (dkdv_work, lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)])
+    if sched == "halves":
+        # dQ: both halves' bins on two streams (bin 0 overwrites a half's rows, the others
+        # add); dK/dV: one group of nb launches on this stream
+        T.run("bwd_dq", dq_work, dq_halves, launches=2 * nb)
+        T.run("bwd_dkdv", dkdv_work, lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)], launches=nb)
+    elif sched == "serial":
+        T.run("bwd_dq", dq_work, dq_bins, launches=nb)
+        T.run("bwd_dkdv", dkdv_work, lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)], launches=nb)
+    else:
+        # overlap: the dQ phase of every bin on the side stream beside the dK/dV phase of
+        # every bin on this stream (they write disjoint buffers and read the same inputs)
+        P["ev_fork_dq"].record(main)
+        side.wait_event(P["ev_fork_dq"])
+        with torch.cuda.stream(side):
+            T.run("bwd_dq", dq_work, dq_bins, launches=nb, stream=side)
+        T.run("bwd_dkdv", dkdv_work, lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)], launches=nb)
+        P["ev_join_dq"].record(side)
+        main.wait_event(P["ev_join_dq"])
     return bins_np, load.numpy(), cost_np, bin_pairs
 
 
@@ -760,6 +789,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split", action="store_true",
                     help="run the step's forwards and dQ phases on the split schedule")
+    ap.add_argument("--bwd-schedule", choices=("halves", "serial", "overlap"), default="overlap",
+                    help="backward phases of the step: dQ in two halves of the blocks on two "
+                         "streams then dK/dV (halves); dQ then dK/dV on one stream (serial); "
+                         "dQ on a second stream beside dK/dV (overlap)")
     ap.add_argument("--balance", metavar="WORKLOAD",
                     help="instead of the benchmark, the per-bin balance study of a workload "
                          "with bins (fwdbwd_bf16_8kq_64k or cp64_share_8kq_512k)")
@@ -798,7 +831,7 @@ def main():
               flush=True)
         return
     log("building the synthetic workload ...")
-    P = build_problem(torch, args.seed, split=args.split)
+    P = build_problem(torch, args.seed, split=args.split, bwd_schedule=args.bwd_schedule)
     w = P["w"]
     T = Timers(torch)
     log(f"warmup {args.warmup} steps ...")
@@ -845,7 +878,34 @@ def main():
     roofline = {"bound": "mfma" if is_mfma else "hbm", "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s" if is_mfma else "GB/s",
                 "frac": round(achieved / peak, 4), "traffic": recorded_traffic(dom), "kernel": dom,
-                "avg_launch_ms": round(avg_ms, 4), "launches_per_step": a["launches"] // args.steps}
+                "avg_launch_ms": round(avg_ms, 4), "launches_per_step": a["launches"] // args.steps,
+                "measured": "HIP events around the phase's launches in the timed steps"}
+    if args.bwd_schedule == "overlap" and dom == "bwd_dkdv":
+        # In the step the dK/dV launches share the GPU with the dQ phase on the second
+        # stream, so their event time is not the kernel's own: the roofline takes the
+        # same launches run alone right after the timed steps, and keeps the in-step
+        # figure beside it.
+        reps = 5
+        work, fn = P["dkdv_phase"]
+        T2 = Timers(torch)
+        T2.reserve(reps)
+        T2.only = "all"
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            T2.run("bwd_dkdv", work, fn, launches=w.n_bin)
+        torch.cuda.synchronize()
+        b2 = T2.summary()["bwd_dkdv"]
+        iso_ms = b2["ms"] / b2["launches"]
+        iso = b2["work"] / b2["launches"] / (iso_ms * 1e-3) / 1e12
+        roofline["in_step"] = {"achieved": roofline["achieved"], "frac": roofline["frac"],
+                               "avg_launch_ms": roofline["avg_launch_ms"]}
+        roofline.update({"achieved": round(iso, 2), "frac": round(iso / peak, 4),
+                         "avg_launch_ms": round(iso_ms, 4),
+                         "measured": f"HIP events around the step's {w.n_bin} dK/dV calls (count, "
+                                     f"scan, main and fix-up kernels each) run alone {reps} times "
+                                     "right after the timed steps; in_step: the same launches "
+                                     "inside the timed steps, beside the dQ phase on a second "
+                                     "stream"})
     kernels = {}   # from the warm-up steps with events around every phase
     n_bd = max(args.warmup - 1, 1)
     for n, k in per_kernel.items():
@@ -862,6 +922,7 @@ def main():
                    "hkv": w.hkv, "head_dim": w.d, "block": 16, "chunks": w.n_chunk,
                    "chunk_size": w.chunk_size, "bins": w.n_bin, "seed": args.seed,
                    "row_group_schedule": "split" if args.split else "ranked",
+                   "bwd_schedule": args.bwd_schedule,
                    "allowed_pairs_per_head": pairs, "pct_of_bf16_peak": round(
                        100 * value / PEAK_BF16_TFLOPS, 2),
                    "lpt_imbalance": round(float(load.max() / load.mean() - 1), 5)},
@@ -869,8 +930,11 @@ def main():
         "kernels": kernels,
         "kernels_note": f"per-phase times from {n_bd} warm-up steps with events around every phase; "
                         "gather_fwd is the bins' context gathers and forwards on two streams, its "
-                        "rate the forward's FLOP over that span; bwd_dq runs two halves of the "
-                        "query blocks on two streams",
+                        "rate the forward's FLOP over that span; " + {
+                            "halves": "bwd_dq runs two halves of the query blocks on two streams",
+                            "serial": "bwd_dq then bwd_dkdv on one stream",
+                            "overlap": "bwd_dq runs on a second stream beside bwd_dkdv, so their "
+                                       "spans overlap"}[args.bwd_schedule],
     }
     # the combine one device performs at context-parallel size 64 (the 8192-query view,
     # 64 bf16 partials), every partial live and with the real empty pattern

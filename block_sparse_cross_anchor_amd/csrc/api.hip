@@ -213,8 +213,10 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
                       sample_start, chunk_gstart, chunk_len, n_chunk, n_loc, k_self, v_self, a);
   if (st != SXA_OK) return st;
   constexpr int32_t kAll = SXA_BWD_DELTA | SXA_BWD_DQ | SXA_BWD_DKDV;
-  if (flags == 0) flags = kAll;
-  if (flags & ~(kAll | SXA_BWD_DQ_OVERWRITE)) return fail(SXA_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & kAll) == 0) flags |= kAll;  // no phase named: every phase
+  if (flags & ~(kAll | SXA_BWD_DQ_OVERWRITE | SXA_BWD_DKDV_BF16)) return fail(SXA_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & SXA_BWD_DKDV_BF16) && in_dtype != SXA_BF16)
+    return fail(SXA_EUNSUPPORTED, "bf16 key/value gradients need bf16 inputs");
   if (n_blk > 0 && (o == nullptr || dout == nullptr || lse == nullptr || delta_ws == nullptr))
     return fail(SXA_EINVAL, "o, dout, lse and delta_ws must not be NULL");
   if (n_blk > 0 && (flags & SXA_BWD_DQ) && dq_accum == nullptr)
@@ -250,7 +252,7 @@ int sparse_xattn_bwd(const void* q, const void* k, const void* v, sxa_dtype in_d
   if (n_blk == 0) {
     if (!(flags & SXA_BWD_DKDV)) return ok();
     // no query: the gradients of the local keys/values are zero
-    const int64_t kv_words = n_loc * hkv * d;  // float32 gradients
+    const int64_t kv_words = n_loc * hkv * d / ((flags & SXA_BWD_DKDV_BF16) ? 2 : 1);  // 32-bit words
     hipError_t e = sxa::launch_zero_words(dk, kv_words, s);
     if (e == hipSuccess) e = sxa::launch_zero_words(dv, kv_words, s);
     return hip_status(e, "sparse_xattn_bwd zero fill");

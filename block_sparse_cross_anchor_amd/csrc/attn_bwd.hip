@@ -48,10 +48,10 @@ struct BwdParams {
   const float* lse;
   const float* delta;  // [2][n_q][hq]: delta rows, then lse * log2(e) (+inf where lse = -inf)
   float* dq;
-  float* dk;
-  float* dv;
-  float* dk_self;
-  float* dv_self;
+  void* dk;  // float32, or bf16 with grad_bf16
+  void* dv;
+  void* dk_self;
+  void* dv_self;
   const int32_t* anchor;
   const int32_t* sample_start;
   const int32_t* chunk_gstart;
@@ -61,6 +61,7 @@ struct BwdParams {
   float scale;
   float scale_log2;  // scale * log2(e)
   int32_t dq_overwrite;
+  int32_t grad_bf16;  // dK, dV (and own-block) written as bf16, rounded to nearest even
   const int32_t* rg_order;  // dQ: row group of workgroup blockIdx / hkv (nullptr: identity)
   // split dQ (jobs != nullptr): job blockIdx / hkv = {row group, first tile, end tile,
   // slot}; a job with a slot writes its scaled dQ sum there instead of adding it
@@ -78,6 +79,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   v[0] = static_cast<__bf16>(a);
   v[1] = static_cast<__bf16>(b);
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Four gradient values to element offset `o` of a float32 or bf16 gradient tensor.
+__device__ __forceinline__ void store_grad4(void* base, int64_t o, const f32x4& x, bool bf16) {
+  if (bf16)
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + o) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  else
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + o) = x;
 }
 
 // ============================================================================ dq kernel
@@ -211,58 +220,61 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
       const bool all_full = __all(full);
       const uint32_t base = lds_addr(bufs[cb]);
       const uint32_t kb = base + f_k, ta = base + t_a, tb = base + t_b;
-      f32x16 sacc[2], pacc[2];
+      // The tile's two 32-key halves one after the other: S^T and dP^T of half mt
+      // (16 MFMAs), its dS^T (VALU), then the dQ^T MFMAs of its two 16-key steps.
+      // Only one half's S^T, dP^T accumulators are live at a time, which leaves the
+      // registers for reading every LDS fragment one MFMA pair ahead of its use; and
+      // the exponent of half 0 has half 1's MFMAs to overlap with.
+      bf16x8 kf = lds_frag(kb), vf = lds_frag(kb + kVOff);
+      bf16x8 kt = lds_frag_t(ta, tb);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x16 sacc, pacc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[mt][i] = pacc[mt][i] = 0.f;
+        for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t o = kb ^ (32 * ks);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 kf = lds_frag(o + mt * 64 * D);
-          const bf16x8 vf = lds_frag(o + mt * 64 * D + kVOff);
-          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
-          pacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[ks], pacc[mt], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 ck = kf, cv = vf;
+          const int nx = mt * KS + ks + 1;  // next (half, k-step)
+          if (nx < 2 * KS) {
+            const uint32_t o = (kb ^ (32 * (nx % KS))) + (nx / KS) * 64 * D;
+            kf = lds_frag(o);
+            vf = lds_frag(o + kVOff);
+          }
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ck, qf[ks], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cv, df[ks], pacc, 0, 0, 0);
         }
-      }
-      // exponent in place; keys outside the row's interval get exp2(-inf) = 0
+        // exponent in place; keys outside the row's interval get exp2(-inf) = 0
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[mt][i] = fmaf(sacc[mt][i], p.scale_log2, -lse2);
-      if (!all_full) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(sacc[i], p.scale_log2, -lse2);
+        if (!all_full) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = 32 * mt + 8 * (i / 4) + 4 * h2 + (i % 4);
-            if (key < a_lo || key >= a_hi) sacc[mt][i] = -INFINITY;
+            if (key < a_lo || key >= a_hi) sacc[i] = -INFINITY;
           }
-      }
-      u32x4 dsw[4];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        }
+        u32x4 dsw[2];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const int i = 2 * q;
-          const float d0 = __builtin_amdgcn_exp2f(sacc[mt][i]) * (pacc[mt][i] - dlt);
-          const float d1 = __builtin_amdgcn_exp2f(sacc[mt][i + 1]) * (pacc[mt][i + 1] - dlt);
-          dsw[2 * mt + q / 4][q % 4] = pack_bf16x2(d0, d1);
+          const float d0 = __builtin_amdgcn_exp2f(sacc[2 * q]) * (pacc[2 * q] - dlt);
+          const float d1 = __builtin_amdgcn_exp2f(sacc[2 * q + 1]) * (pacc[2 * q + 1] - dlt);
+          dsw[q / 4][q % 4] = pack_bf16x2(d0, d1);
         }
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint32_t oa = (ta ^ (64 * dt)) + kq * 32 * D, ob = (tb ^ (64 * dt)) + kq * 32 * D;
-          const bf16x8 kt = lds_frag_t(oa, ob);
-          dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, __builtin_bit_cast(bf16x8, dsw[kq]), dqacc[dt], 0,
-                                                              0, 0);
+        for (int j = 0; j < 2 * DT; ++j) {
+          const int kq = 2 * mt + j / DT, dt = j % DT;
+          const bf16x8 ck = kt;
+          const int nx = 2 * DT * mt + j + 1;  // next (16-key step, d tile)
+          if (nx < 4 * DT) {
+            const int kq1 = nx / DT, dt1 = nx % DT;
+            kt = lds_frag_t((ta ^ (64 * dt1)) + kq1 * 32 * D, (tb ^ (64 * dt1)) + kq1 * 32 * D);
+          }
+          dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ck, __builtin_bit_cast(bf16x8, dsw[kq % 2]),
+                                                              dqacc[dt], 0, 0, 0);
         }
       }
     }
-
     if (!have1) break;
     cur = n1;
     n1 = n2;
@@ -906,8 +918,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
                                   dvacc[hh][dt][4 * jj + 3]};
           if (whole) {
             const int64_t o = ((krow0 + krow[hh]) * p.hkv + g) * D + dcol;
-            *reinterpret_cast<f32x4*>((self_tile ? p.dk_self : p.dk) + o) = kv4 * p.scale;
-            *reinterpret_cast<f32x4*>((self_tile ? p.dv_self : p.dv) + o) = vv4;
+            store_grad4(self_tile ? p.dk_self : p.dk, o, kv4 * p.scale, p.grad_bf16);
+            store_grad4(self_tile ? p.dv_self : p.dv, o, vv4, p.grad_bf16);
           } else {
             *reinterpret_cast<f32x4*>(slot + (krow[hh] * 2 + 0) * D + dcol) = kv4;
             *reinterpret_cast<f32x4*>(slot + (krow[hh] * 2 + 1) * D + dcol) = vv4;
@@ -934,8 +946,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, DkdvSched
   const int64_t n_q = static_cast<int64_t>(p.n_blk) * kBlock;
   const int64_t key_rows = self_tile ? n_q : p.n_loc;
   const int64_t krow0 = static_cast<int64_t>(self_tile ? t - sc.n_ctx_tiles : t) * kKeysPerWG;
-  float* dK = self_tile ? p.dk_self : p.dk;
-  float* dV = self_tile ? p.dv_self : p.dv;
+  void* dK = self_tile ? p.dk_self : p.dk;
+  void* dV = self_tile ? p.dv_self : p.dv;
   const int64_t W = ld_uniform(sc.prefix, sc.n_tiles);
   const int t0 = ld_uniform(sc.prefix, t);
   const int hits = sc.tinfo[t].z;
@@ -966,7 +978,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, DkdvSched
         if ((j + 1) * tot / ns > j * tot / ns)  // empty shares (list shorter than the grid) wrote nothing
           acc += *reinterpret_cast<const f32x4*>(sc.slots + 2 * j * slot_elems + e);
     }
-    *reinterpret_cast<f32x4*>((which == 0 ? dK : dV) + (kr * p.hkv + g) * D + dcol) = which == 0 ? acc * p.scale : acc;
+    store_grad4(which == 0 ? dK : dV, (kr * p.hkv + g) * D + dcol, which == 0 ? acc * p.scale : acc, p.grad_bf16);
   }
 }
 
@@ -1005,10 +1017,11 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   p.lse = a.lse_in;
   p.delta = a.delta;
   p.dq = a.dq;
-  p.dk = static_cast<float*>(a.dk);
-  p.dv = static_cast<float*>(a.dv);
-  p.dk_self = static_cast<float*>(a.dk_self);
-  p.dv_self = static_cast<float*>(a.dv_self);
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.dk_self = a.dk_self;
+  p.dv_self = a.dv_self;
+  p.grad_bf16 = (a.flags & SXA_BWD_DKDV_BF16) != 0;
   p.anchor = a.anchor;
   p.sample_start = a.sample_start;
   p.chunk_gstart = a.chunk_gstart;

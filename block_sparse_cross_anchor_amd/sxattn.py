@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libsxattn.so")
 
 SXA_F32, SXA_BF16 = 0, 1
 SXA_OK, SXA_EINVAL, SXA_EUNSUPPORTED, SXA_EHIP = 0, -1, -2, -3
-BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_DQ_OVERWRITE = 1, 2, 4, 8
+BWD_DELTA, BWD_DQ, BWD_DKDV, BWD_DQ_OVERWRITE, BWD_DKDV_BF16 = 1, 2, 4, 8, 16
 BLOCK = 16
 
 EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_fwd_noalloc", "sparse_xattn_fwd_workspace_bytes",
@@ -227,12 +227,14 @@ def bwd_workspace(n_blk: int, n_loc: int, hq: int, hkv: int, d: int, device, spl
 
 def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
                      k_self=None, v_self=None, delta_ws=None, dk=None, dv=None, dk_self=None,
-                     dv_self=None, flags: int = 0, workspace="auto"):
+                     dv_self=None, flags: int = 0, workspace="auto", grad_dtype=None):
     """Backward of the local chunks (+ own-block term).  Adds into dq_accum (float32)
-    unless BWD_DQ_OVERWRITE is set; ``flags`` selects phases (0 = all).  ``workspace``:
-    "auto" (cached scratch: load-balanced phases), "split" (also the split dQ
-    schedule), None, or a device tensor.
-    Returns the float32 gradients (dk, dv, dk_self, dv_self)."""
+    unless BWD_DQ_OVERWRITE is set; ``flags`` selects phases (none named = all).
+    ``workspace``: "auto" (cached scratch: load-balanced phases), "split" (also the
+    split dQ schedule), None, or a device tensor.  The key/value gradients are float32
+    or bf16: the dtype of the given dk (``grad_dtype``, default float32, when dk is
+    not given); bf16 sets BWD_DKDV_BF16.
+    Returns the gradients (dk, dv, dk_self, dv_self)."""
     n_q, hq, d = q.shape
     hkv = k.shape[1]
     _need(q, "q")
@@ -245,22 +247,26 @@ def sparse_xattn_bwd(q, k, v, meta: Meta, scale: float, o, dout, lse, dq_accum,
     if delta_ws is None:
         delta_ws = torch.empty((2, n_q, hq), dtype=torch.float32, device=q.device)
     _need(delta_ws, "delta_ws", (2, n_q, hq), torch.float32)
-    f32 = torch.float32
+    gd = dk.dtype if dk is not None else (grad_dtype or torch.float32)
+    if gd not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"key/value gradients must be float32 or bfloat16, not {gd}")
     if dk is None:
-        dk = torch.empty(k.shape, dtype=f32, device=k.device)
+        dk = torch.empty(k.shape, dtype=gd, device=k.device)
     if dv is None:
-        dv = torch.empty(v.shape, dtype=f32, device=v.device)
-    _need(dk, "dk", k.shape, f32)
-    _need(dv, "dv", v.shape, f32)
+        dv = torch.empty(v.shape, dtype=gd, device=v.device)
+    _need(dk, "dk", k.shape, gd)
+    _need(dv, "dv", v.shape, gd)
     if k_self is not None:
         _need(k_self, "k_self", (n_q, hkv, d), q.dtype)
         _need(v_self, "v_self", (n_q, hkv, d), q.dtype)
         if dk_self is None:
-            dk_self = torch.empty(k_self.shape, dtype=f32, device=q.device)
+            dk_self = torch.empty(k_self.shape, dtype=gd, device=q.device)
         if dv_self is None:
-            dv_self = torch.empty(v_self.shape, dtype=f32, device=q.device)
-        _need(dk_self, "dk_self", k_self.shape, f32)
-        _need(dv_self, "dv_self", v_self.shape, f32)
+            dv_self = torch.empty(v_self.shape, dtype=gd, device=q.device)
+        _need(dk_self, "dk_self", k_self.shape, gd)
+        _need(dv_self, "dv_self", v_self.shape, gd)
+    if gd == torch.bfloat16:
+        flags = int(flags) | BWD_DKDV_BF16
     lib = load_library()
     if isinstance(workspace, str):
         if workspace not in ("auto", "split"):

@@ -23,7 +23,7 @@
  *   q, o, dout, dq_accum : [n_q][hq][d]
  *   k, v, dk, dv          : [n_loc][hkv][d]   local rows = the listed chunks back to back
  *   k_self, v_self, dk_self, dv_self : [n_q][hkv][d]  keys/values of the draft tokens
- *   (gradients dq_accum, dk, dv, dk_self, dv_self are always float32)
+ *   (gradients are float32; dk, dv, dk_self, dv_self may be bf16, see sparse_xattn_bwd)
  *   lse                   : [n_q][hq] float32
  *   delta_ws              : [2][n_q][hq] float32
  * Query head h reads kv head h / (hq / hkv).
@@ -135,12 +135,14 @@ int64_t sparse_xattn_fwd_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv)
  * beyond 4096 row groups of 256 query rows per kv head, where no split is done. */
 int64_t sparse_xattn_fwd_split_workspace_bytes(int32_t n_blk, int32_t hq, int32_t hkv, int32_t d);
 
-/* Phases of sparse_xattn_bwd (bit flags; 0 means all of DELTA | DQ | DKDV). */
+/* Phases of sparse_xattn_bwd (bit flags; naming none of DELTA, DQ, DKDV means all
+ * three) and their modifiers. */
 enum {
   SXA_BWD_DELTA = 1,         /* pre-pass: delta_ws = (rowsum(dout * o), lse * log2 e) */
   SXA_BWD_DQ = 2,            /* add this call's query gradient to dq_accum */
   SXA_BWD_DKDV = 4,          /* write dk, dv (and dk_self, dv_self) */
-  SXA_BWD_DQ_OVERWRITE = 8   /* with SXA_BWD_DQ: overwrite dq_accum instead of adding */
+  SXA_BWD_DQ_OVERWRITE = 8,  /* with SXA_BWD_DQ: overwrite dq_accum instead of adding */
+  SXA_BWD_DKDV_BF16 = 16     /* with SXA_BWD_DKDV: dk, dv, dk_self, dv_self are bf16 */
 };
 
 /*
@@ -154,9 +156,11 @@ enum {
  *            with the same o, dout and lse may skip the phase.
  *   dq_accum [n_q][hq][d] float32: this call's query gradient is ADDED to it (or
  *            written, with SXA_BWD_DQ_OVERWRITE), so per-chunk calls accumulate.
- *   dk, dv   [n_loc][hkv][d] float32: overwritten.
- *   dk_self, dv_self [n_q][hkv][d] float32: overwritten when k_self != NULL
- *            (must then be non-NULL), ignored otherwise.
+ *   dk, dv   [n_loc][hkv][d] float32 (bf16 with SXA_BWD_DKDV_BF16, bf16 inputs
+ *            only): overwritten.  The sums are formed in float32 either way; the
+ *            bf16 form rounds each final value to nearest even.
+ *   dk_self, dv_self [n_q][hkv][d] float32 (bf16 with SXA_BWD_DKDV_BF16): overwritten
+ *            when k_self != NULL (must then be non-NULL), ignored otherwise.
  *   workspace, workspace_bytes: optional device scratch for the bf16 dK/dV phase.
  *            With at least sparse_xattn_bwd_workspace_bytes() bytes the phase is
  *            load-balanced: one workgroup per compute unit, each taking an equal

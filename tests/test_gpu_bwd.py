@@ -290,3 +290,49 @@ def test_bwd_split_key_tiles_match_unsplit():
     assert np.abs(r[1]).max() > 0
     assert rel_frob(host64(r_split[0])[rows], r[1]) <= 3e-2
     assert rel_frob(host64(r_split[1])[rows], r[2]) <= 3e-2
+
+
+@pytest.mark.parametrize("workspace", [None, "auto"])
+def test_bwd_bf16_key_value_gradients(workspace):
+    """SXA_BWD_DKDV_BF16: the key/value gradients (context and own-block) written as
+    bf16 are the round-to-nearest-even of the float32 results of the same schedule
+    (the sums are formed in float32 either way), and within the gradient bound of the
+    oracle; on both the per-tile and the load-balanced (stream-K) dK/dV schedules, on
+    ragged non-contiguous chunks."""
+    w = W["fwd_bf16_512q_4k"]
+    seed = 13
+    meta = synth.meta_for(w, seed)
+    gs = np.array([3072, 0, 1024], np.int32)
+    gl = np.array([1000, 1024, 1024], np.int32)
+    inp = synth.draw_inputs(seed, meta, w.hq, w.hkv, w.d, "bf16", w.std(), gs, gl, with_dout=True)
+    scale = 1.0 / math.sqrt(w.d)
+    dm = device_meta(meta, gs, gl)
+    o, lse = gpu_fwd_merged(meta, inp, scale, dm)
+    args = (dev(inp.q), dev(inp.k), dev(inp.v), dm, scale, o, dev(inp.dout), lse)
+    ks, vs = dev(inp.k_self), dev(inp.v_self)
+    dq32 = torch.zeros(inp.q.shape, dtype=torch.float32, device="cuda")
+    g32 = sxattn.sparse_xattn_bwd(*args, dq32, ks, vs, workspace=workspace)
+    dq16 = torch.zeros(inp.q.shape, dtype=torch.float32, device="cuda")
+    g16 = sxattn.sparse_xattn_bwd(*args, dq16, ks, vs, workspace=workspace,
+                                  grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(dq16, dq32)
+    ro, rl = oracle_merged(meta, inp, scale, gs, gl)
+    r = oracle.sparse_xattn_bwd(inp.q.f64, inp.k.f64, inp.v.f64, ro, inp.dout.f64, rl,
+                                meta.anchor, meta.sample_start, gs, gl, scale,
+                                inp.k_self.f64, inp.v_self.f64)
+    for a, b, want, name in zip(g16, g32, r[1:], ("dk", "dv", "dk_self", "dv_self")):
+        assert a.dtype == torch.bfloat16 and b.dtype == torch.float32
+        assert torch.equal(a, b.to(torch.bfloat16)), name
+        assert rel_frob(host64(a), want) <= 3e-2, name
+    # no queries: bf16 zeros
+    k = torch.randn(100, 2, 128, device="cuda").to(torch.bfloat16)
+    m0 = sxattn.Meta(np.zeros(0, np.int32), np.zeros(0, np.int32), [0], [100])
+    q0 = torch.zeros(0, 4, 128, device="cuda", dtype=torch.bfloat16)
+    dk, dv, _, _ = sxattn.sparse_xattn_bwd(q0, k, k, m0, 0.1, q0, q0,
+                                           torch.zeros(0, 4, device="cuda"),
+                                           torch.zeros(0, 4, 128, device="cuda"),
+                                           dk=torch.full(k.shape, 3.0, device="cuda").to(torch.bfloat16),
+                                           dv=torch.full(k.shape, 3.0, device="cuda").to(torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)

@@ -4,8 +4,8 @@ One pass of the hot path on the 8192-query x 65536-token workload (Hq 32, Hkv 8,
 d 128, bf16) in exactly the launch configuration the benchmark times: chunk costs,
 the LPT plan onto 8 bins, each bin's gather and forward (the bins alternating
 between two streams), the 8-way combine, the delta pre-pass, the dQ phase of every
-bin (accumulated; two halves of the query blocks on two streams) and the
-load-balanced dK/dV phase of every bin.
+bin (accumulated, on a second stream) beside the load-balanced dK/dV phase of every
+bin.
 
 * Values ~ N(0, 1)/sqrt(d) (the workload's own): sampled outputs against the oracle,
   which evaluates each of them from the inputs alone (its backward consumes its own
