@@ -209,19 +209,23 @@ def build_problem(torch, seed, split=False, inputs=None, bwd_schedule="overlap")
             "tok": slice(16 * b0, 16 * b1), "metas": hm,
             "delta": torch.empty((2, 16 * (b1 - b0), hq), dtype=f32, device="cuda"),
             "ws": torch.empty((max(bws, 256),), dtype=torch.uint8, device="cuda")})
+    bws = int(lib.sparse_xattn_bwd_split_workspace_bytes(w.n_anchor, n_loc, hq, hkv, d) if split
+              else lib.sparse_xattn_bwd_workspace_bytes(w.n_anchor, n_loc, hq, hkv, d))
+    P["bwd_ws"] = [torch.empty((max(bws, 256),), dtype=torch.uint8, device="cuda") for _ in range(2)]
     fws = int(lib.sparse_xattn_fwd_split_workspace_bytes(w.n_anchor, hq, hkv, d) if split
               else lib.sparse_xattn_fwd_workspace_bytes(w.n_anchor, hq, hkv))
     P["fwd_ws"] = [torch.empty((max(fws, 256),), dtype=torch.uint8, device="cuda") for _ in range(2)]
     return P
 
 
-def step(torch, P, T):
-    """One pass of the hot path; returns the host-side plan (bins, load, cost)."""
+def plan(torch, P, T):
+    """Steps 1 and 2 of the hot path: the GPU cost of every chunk, copied to the host,
+    the host LPT plan, and its upload into the device plan buffers that every later
+    launch reads.  Returns (bins, load, cost, chunks of each bin) on the host."""
     from block_sparse_cross_anchor_amd import sxattn
 
     w = P["w"]
-    nb, per_bin, n_loc, d, hq = w.n_bin, P["per_bin"], P["n_loc"], w.d, w.hq
-    scale = P["scale"]
+    nb, per_bin = w.n_bin, P["per_bin"]
     T.run("chunk_cost", 8 * w.n_anchor + 8 * w.n_chunk,
           lambda: sxattn.chunk_cost(P["anchor"], P["start"], w.n_ctx, w.chunk_size, out=P["cost"]))
     # device -> host; the host polls the copy's event instead of blocking in the copy,
@@ -240,7 +244,49 @@ def step(torch, P, T):
     # the host buffer is next written after the next step's cost copy, which waits
     # for this copy
     P["plan"].copy_(P["plan_h"], non_blocking=True)
-    cost_np = cost.numpy()
+    return bins_np, load, cost.numpy(), order
+
+
+def step(torch, P, T):
+    """One pass of the hot path; returns the host-side plan (bins, load, cost) and the
+    allowed pairs of each bin.  With a captured graph (P["graph"]) the launches after
+    the plan upload are one replay of it."""
+    bins_np, load, cost_np, order = plan(torch, P, T)
+    if P.get("graph") is not None:
+        P["graph"].replay()
+        bin_pairs = [int(cost_np[order[b]].sum()) for b in range(P["w"].n_bin)]
+    else:
+        bin_pairs = post_plan(torch, P, T, bins_np, cost_np, order)
+    return bins_np, load.numpy(), cost_np, bin_pairs
+
+
+def capture_graph(torch, P):
+    """Capture the launches of a step after its plan upload (gathers, forwards,
+    combine, delta, dQ and dK/dV phases on both streams) into one HIP graph.  They
+    read the plan from the device buffers every replay rewrites, so one capture serves
+    every step; the capture itself runs nothing."""
+    bins_np, _, cost_np, order = plan(torch, P, _NoTimer())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        post_plan(torch, P, _NoTimer(), bins_np, cost_np, order)
+    torch.cuda.synchronize()
+    P["graph"] = g
+
+
+class _NoTimer:
+    def run(self, name, work, fn, launches=1, stream=None):
+        return fn()
+
+
+def post_plan(torch, P, T, bins_np, cost_np, order):
+    """Steps 3 to 5 of the hot path, enqueued on the current stream and the side
+    stream; returns the allowed context pairs of each bin."""
+    from block_sparse_cross_anchor_amd import sxattn
+
+    w = P["w"]
+    nb, n_loc, d, hq = w.n_bin, P["n_loc"], w.d, w.hq
+    scale = P["scale"]
     self_pairs = 16 * w.n_q
     metas = P["metas"]
     main, side = torch.cuda.current_stream(), P["side_stream"]
@@ -296,7 +342,7 @@ def step(torch, P, T):
     def whole_delta():
         sxattn.sparse_xattn_bwd(P["q"], P["k_loc"][0], P["v_loc"][0], metas[0], scale, o, P["do"],
                                 lse, P["dq"], delta_ws=P["delta"], dk=P["dk_loc"][0],
-                                dv=P["dv_loc"][0], flags=sxattn.BWD_DELTA)
+                                dv=P["dv_loc"][0], flags=sxattn.BWD_DELTA, workspace=None)
 
     def deltas():   # the whole rows (for dK/dV), then each dQ half's own
         whole_delta()
@@ -327,39 +373,47 @@ def step(torch, P, T):
         P["ev_join_dq"].record(side)
         main.wait_event(P["ev_join_dq"])
 
-    def bwd(b, flags):
+    def bwd(b, flags, ws):
         self_kv = (P["ks"], P["vs"]) if b == 0 else (None, None)
         sxattn.sparse_xattn_bwd(
             P["q"], P["k_loc"][b], P["v_loc"][b], metas[b], scale, o, P["do"], lse, P["dq"],
             self_kv[0], self_kv[1], delta_ws=P["delta"], dk=P["dk_loc"][b], dv=P["dv_loc"][b],
-            dk_self=P["dks"], dv_self=P["dvs"], flags=flags)
+            dk_self=P["dks"], dv_self=P["dvs"], flags=flags, workspace=ws)
 
-    def dq_bins():
+    # one workspace per stream: the dK/dV phase's on this stream, the dQ phase's on the
+    # side stream when the two overlap
+    ws_main, ws_side = P["bwd_ws"]
+
+    def dq_bins(ws):
         for b in range(nb):
-            bwd(b, sxattn.BWD_DQ | (sxattn.BWD_DQ_OVERWRITE if b == 0 else 0))
+            bwd(b, sxattn.BWD_DQ | (sxattn.BWD_DQ_OVERWRITE if b == 0 else 0), ws)
+
+    def dkdv_bins():
+        for b in range(nb):
+            bwd(b, sxattn.BWD_DKDV, ws_main)
 
     dq_work, dkdv_work = 6.0 * d * hq * all_pairs, 8.0 * d * hq * all_pairs
     # the dK/dV phase alone (same inputs and plan), for its roofline outside the step
-    P["dkdv_phase"] = (dkdv_work, lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)])
+    P["dkdv_phase"] = (dkdv_work, dkdv_bins)
     if sched == "halves":
         # dQ: both halves' bins on two streams (bin 0 overwrites a half's rows, the others
         # add); dK/dV: one group of nb launches on this stream
         T.run("bwd_dq", dq_work, dq_halves, launches=2 * nb)
-        T.run("bwd_dkdv", dkdv_work, lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)], launches=nb)
+        T.run("bwd_dkdv", dkdv_work, dkdv_bins, launches=nb)
     elif sched == "serial":
-        T.run("bwd_dq", dq_work, dq_bins, launches=nb)
-        T.run("bwd_dkdv", dkdv_work, lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)], launches=nb)
+        T.run("bwd_dq", dq_work, lambda: dq_bins(ws_main), launches=nb)
+        T.run("bwd_dkdv", dkdv_work, dkdv_bins, launches=nb)
     else:
         # overlap: the dQ phase of every bin on the side stream beside the dK/dV phase of
         # every bin on this stream (they write disjoint buffers and read the same inputs)
         P["ev_fork_dq"].record(main)
         side.wait_event(P["ev_fork_dq"])
         with torch.cuda.stream(side):
-            T.run("bwd_dq", dq_work, dq_bins, launches=nb, stream=side)
-        T.run("bwd_dkdv", dkdv_work, lambda: [bwd(b, sxattn.BWD_DKDV) for b in range(nb)], launches=nb)
+            T.run("bwd_dq", dq_work, lambda: dq_bins(ws_side), launches=nb, stream=side)
+        T.run("bwd_dkdv", dkdv_work, dkdv_bins, launches=nb)
         P["ev_join_dq"].record(side)
         main.wait_event(P["ev_join_dq"])
-    return bins_np, load.numpy(), cost_np, bin_pairs
+    return bin_pairs
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_8kq_64k_8bins.md")
@@ -789,6 +843,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split", action="store_true",
                     help="run the step's forwards and dQ phases on the split schedule")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="enqueue every launch of the timed steps from the host instead of "
+                         "replaying the captured graph of the post-plan launches")
     ap.add_argument("--bwd-schedule", choices=("halves", "serial", "overlap"), default="overlap",
                     help="backward phases of the step: dQ in two halves of the blocks on two "
                          "streams then dK/dV (halves); dQ then dK/dV on one stream (serial); "
@@ -847,13 +904,11 @@ def main():
         T.pending = []
     else:
         per_kernel = {}
-    # the dominant phase: the most time per step in the breakdown (the backward's
-    # dK/dV phase when there is no breakdown), among the phases whose launches run
-    # one after another on one stream (so that a launch's events time that kernel)
-    single = {n: k for n, k in per_kernel.items() if n not in ("gather_fwd", "bwd_dq")}
-    dom = max(single, key=lambda n: single[n]["ms"]) if single else "bwd_dkdv"
-    T.reserve(per_step[dom] * args.steps)
-    T.only = dom
+    T.only = None
+    if not args.no_graph:
+        log("capturing the step's launches after the plan upload into a HIP graph ...")
+        capture_graph(torch, P)
+        step(torch, P, T)   # first replay, untimed
     log(f"timing {args.steps} steps ...")
     gc.collect()
     gc.disable()   # no collector pause inside the timed region
@@ -869,43 +924,40 @@ def main():
     pairs = ctx_pairs + 16 * w.n_q
     flop = 14.0 * w.d * w.hq * pairs
     value = flop / (ms_step * 1e-3) / 1e12
-    a = T.summary()[dom]
+    # Roofline of the dominant kernel: the step's dK/dV calls (count, scan, main and
+    # fix-up kernels each) run alone right after the timed steps, with HIP events
+    # around each call, on the same inputs and plan.  Inside the step they share the
+    # GPU with the dQ phase on the second stream (and replay from the graph), so
+    # their own time is measured here; the in-step figure from the warm-up breakdown
+    # is kept beside it.
+    reps = 5
+    work, fn = P["dkdv_phase"]
+    T2 = Timers(torch)
+    T2.reserve(reps)
+    T2.only = "all"
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        T2.run("bwd_dkdv", work, fn, launches=w.n_bin)
+    torch.cuda.synchronize()
+    a = T2.summary()["bwd_dkdv"]
     avg_ms = a["ms"] / a["launches"]
-    work_per_launch = a["work"] / a["launches"]
-    is_mfma = dom in ("sparse_xattn_fwd", "bwd_dq", "bwd_dkdv")
-    achieved = work_per_launch / (avg_ms * 1e-3) / (1e12 if is_mfma else 1e9)
-    peak = PEAK_BF16_TFLOPS if is_mfma else PEAK_HBM_GBS
-    roofline = {"bound": "mfma" if is_mfma else "hbm", "achieved": round(achieved, 2),
-                "peak": peak, "unit": "TFLOP/s" if is_mfma else "GB/s",
-                "frac": round(achieved / peak, 4), "traffic": recorded_traffic(dom), "kernel": dom,
-                "avg_launch_ms": round(avg_ms, 4), "launches_per_step": a["launches"] // args.steps,
-                "measured": "HIP events around the phase's launches in the timed steps"}
-    if args.bwd_schedule == "overlap" and dom == "bwd_dkdv":
-        # In the step the dK/dV launches share the GPU with the dQ phase on the second
-        # stream, so their event time is not the kernel's own: the roofline takes the
-        # same launches run alone right after the timed steps, and keeps the in-step
-        # figure beside it.
-        reps = 5
-        work, fn = P["dkdv_phase"]
-        T2 = Timers(torch)
-        T2.reserve(reps)
-        T2.only = "all"
-        torch.cuda.synchronize()
-        for _ in range(reps):
-            T2.run("bwd_dkdv", work, fn, launches=w.n_bin)
-        torch.cuda.synchronize()
-        b2 = T2.summary()["bwd_dkdv"]
-        iso_ms = b2["ms"] / b2["launches"]
-        iso = b2["work"] / b2["launches"] / (iso_ms * 1e-3) / 1e12
-        roofline["in_step"] = {"achieved": roofline["achieved"], "frac": roofline["frac"],
-                               "avg_launch_ms": roofline["avg_launch_ms"]}
-        roofline.update({"achieved": round(iso, 2), "frac": round(iso / peak, 4),
-                         "avg_launch_ms": round(iso_ms, 4),
-                         "measured": f"HIP events around the step's {w.n_bin} dK/dV calls (count, "
-                                     f"scan, main and fix-up kernels each) run alone {reps} times "
-                                     "right after the timed steps; in_step: the same launches "
-                                     "inside the timed steps, beside the dQ phase on a second "
-                                     "stream"})
+    achieved = a["work"] / a["launches"] / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": recorded_traffic("bwd_dkdv"),
+                "kernel": "bwd_dkdv", "avg_launch_ms": round(avg_ms, 4),
+                "launches_per_step": w.n_bin,
+                "measured": f"HIP events around each of the step's {w.n_bin} dK/dV calls (count, "
+                            f"scan, main and fix-up kernels), run alone {reps} times right after "
+                            "the timed steps on the same inputs and plan"}
+    if "bwd_dkdv" in per_kernel:
+        k = per_kernel["bwd_dkdv"]
+        ms_l = k["ms"] / k["launches"]
+        ach = k["work"] / k["launches"] / (ms_l * 1e-3) / 1e12
+        roofline["in_step"] = {"achieved": round(ach, 2), "frac": round(ach / peak, 4),
+                               "avg_launch_ms": round(ms_l, 4),
+                               "measured": "the same calls inside the warm-up steps (eager, with "
+                                           "events around every phase)"}
     kernels = {}   # from the warm-up steps with events around every phase
     n_bd = max(args.warmup - 1, 1)
     for n, k in per_kernel.items():
@@ -922,7 +974,7 @@ def main():
                    "hkv": w.hkv, "head_dim": w.d, "block": 16, "chunks": w.n_chunk,
                    "chunk_size": w.chunk_size, "bins": w.n_bin, "seed": args.seed,
                    "row_group_schedule": "split" if args.split else "ranked",
-                   "bwd_schedule": args.bwd_schedule,
+                   "bwd_schedule": args.bwd_schedule, "graph": not args.no_graph,
                    "allowed_pairs_per_head": pairs, "pct_of_bf16_peak": round(
                        100 * value / PEAK_BF16_TFLOPS, 2),
                    "lpt_imbalance": round(float(load.max() / load.mean() - 1), 5)},

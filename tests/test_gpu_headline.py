@@ -222,3 +222,25 @@ def test_benchmark_step_boundary_probe_all_outputs():
     for b in range(meta.n_blk):
         r = slice(16 * b, 16 * b + 16)
         assert rel_frob(got_q[r], want_q[r]) <= 3e-2, b
+
+
+def test_benchmark_step_graph_replays_match_eager():
+    """The benchmark replays the launches after the plan upload from one captured HIP
+    graph.  Every replay, with eager work between them (the plan of the next step, and
+    all outputs overwritten with NaN), must reproduce the eager step bit for bit: the
+    kernels are deterministic and read the plan from the device buffers each step
+    rewrites."""
+    P = bench.build_problem(torch, SEED)
+    bench.step(torch, P, _Untimed())
+    torch.cuda.synchronize()
+    names = ("o_parts", "lse_parts", "o", "lse", "delta", "dq", "dk_loc", "dv_loc", "dks", "dvs")
+    want = {k: P[k].clone() for k in names}
+    bench.capture_graph(torch, P)
+    for rep in range(3):
+        for k in names:
+            P[k].fill_(float("nan"))
+        torch.cuda.synchronize()
+        bench.step(torch, P, _Untimed())
+        torch.cuda.synchronize()
+        for k in names:
+            assert torch.equal(P[k], want[k]), (rep, k)
