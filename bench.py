@@ -843,9 +843,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split", action="store_true",
                     help="run the step's forwards and dQ phases on the split schedule")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="enqueue every launch of the timed steps from the host instead of "
-                         "replaying the captured graph of the post-plan launches")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the launches after each step's plan upload from one captured "
+                         "HIP graph instead of enqueuing them from the host")
     ap.add_argument("--bwd-schedule", choices=("halves", "serial", "overlap"), default="overlap",
                     help="backward phases of the step: dQ in two halves of the blocks on two "
                          "streams then dK/dV (halves); dQ then dK/dV on one stream (serial); "
@@ -905,7 +905,7 @@ def main():
     else:
         per_kernel = {}
     T.only = None
-    if not args.no_graph:
+    if args.graph:
         log("capturing the step's launches after the plan upload into a HIP graph ...")
         capture_graph(torch, P)
         step(torch, P, T)   # first replay, untimed
@@ -974,7 +974,7 @@ def main():
                    "hkv": w.hkv, "head_dim": w.d, "block": 16, "chunks": w.n_chunk,
                    "chunk_size": w.chunk_size, "bins": w.n_bin, "seed": args.seed,
                    "row_group_schedule": "split" if args.split else "ranked",
-                   "bwd_schedule": args.bwd_schedule, "graph": not args.no_graph,
+                   "bwd_schedule": args.bwd_schedule, "graph": args.graph,
                    "allowed_pairs_per_head": pairs, "pct_of_bf16_peak": round(
                        100 * value / PEAK_BF16_TFLOPS, 2),
                    "lpt_imbalance": round(float(load.max() / load.mean() - 1), 5)},
