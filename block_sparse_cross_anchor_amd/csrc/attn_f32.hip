@@ -8,11 +8,12 @@
 // natural-log log-sum-exp so that they merge exactly (section "Exchange the
 // smaller side").
 //
-// This path favours plainness over speed: one workgroup per (block, head) walks
-// the block's allowed key ranges in tiles of 64 with float32 VALU dot products and
-// an online softmax.  The backward recomputes probabilities from the merged lse:
-// P = exp(s - lse), dS = P (dO.V - delta), dQ += scale dS K (query-major kernel),
-// dK = scale dS^T Q, dV = P^T dO summed over the group's heads (key-major kernel).
+// One workgroup per (block, head) walks the block's allowed key ranges in tiles of
+// 64; the products run on gfx950's float32 matrix cores (v_mfma_f32_16x16x4_f32:
+// float32 products and sums, so the float32 bound holds), the softmax on the VALU.
+// The backward recomputes probabilities from the merged lse: P = exp(s - lse),
+// dS = P (dO.V - delta), dQ += scale dS K (query-major kernel), dK = scale dS^T Q,
+// dV = P^T dO summed over the group's heads (key-major kernel).
 #include "device_common.h"
 #include "internal.h"
 
@@ -38,61 +39,92 @@ __device__ void for_each_ctx_tile(const AttnArgs& a, int lo, int hi, F&& f) {
   }
 }
 
+// One float32 matrix-core product step, D += A B with A 16x4, B 4x16 (lane l gives
+// A[l % 16][l / 16] and B[l / 16][l % 16]; it holds D[4 (l / 16) + r][l % 16] in r).
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Forward: one workgroup (4 waves) per (block, head), the block's allowed keys in
+// tiles of 64 staged in LDS.  Per tile, wave w forms S^T = K Q^T for keys
+// [16 w, 16 w + 16) on the matrix cores; the online softmax runs on the VALU, 16
+// threads per query row; then O^T += V^T P^T on the matrix cores, each wave owning
+// D / 64 of the 16-column tiles of O^T (so a lane's accumulators are one query's).
 template <int D>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(AttnArgs a) {
-  constexpr int CPT = D / 16;
+  constexpr int TPW = D / 64;  // 16-column tiles of O^T per wave
   const int b = blockIdx.x, h = blockIdx.y;
   const int g = h / (a.hq / a.hkv);
   const int lo = a.sample_start[b], hi = a.anchor[b];
   const float* Q = static_cast<const float*>(a.q);
-  __shared__ float qs[kBlock][D];
+  __shared__ float qs[kBlock][D + 1];
   __shared__ float ks[kTile][D + 1];
-  __shared__ float vs[kTile][D];
-  __shared__ float ss[kBlock][kTile];
+  __shared__ float vs[kTile][D + 1];
+  __shared__ float ps[kBlock][kTile + 1];  // scores, then probabilities
+  __shared__ float alpha_s[kBlock], l_s[kBlock];
   const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, l16 = lane % 16, q4 = lane / 16;
   for (int idx = tid; idx < kBlock * D; idx += kThreads) {
     const int i = idx / D, c = idx % D;
     qs[i][c] = Q[(static_cast<int64_t>(kBlock * b + i) * a.hq + h) * D + c];
   }
-  const int row = tid / 16, cg = tid % 16;
-  float m = -INFINITY, l = 0.f, acc[CPT];
+  const int row = tid / 16, cg = tid % 16;  // softmax: 16 threads per query row
+  float m = -INFINITY, l = 0.f;
+  f32x4 oacc[TPW];
 #pragma unroll
-  for (int u = 0; u < CPT; ++u) acc[u] = 0.f;
+  for (int t = 0; t < TPW; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto process = [&](const float* K, const float* V, int64_t row0, int nrows) {
     __syncthreads();
-    for (int idx = tid; idx < nrows * D; idx += kThreads) {
+    for (int idx = tid; idx < kTile * D; idx += kThreads) {
       const int j = idx / D, c = idx % D;
       const int64_t src = ((row0 + j) * a.hkv + g) * D + c;
-      ks[j][c] = K[src];
-      vs[j][c] = V[src];
+      ks[j][c] = j < nrows ? K[src] : 0.f;  // rows past the tile: finite, masked below
+      vs[j][c] = j < nrows ? V[src] : 0.f;
     }
     __syncthreads();
-    for (int idx = tid; idx < kBlock * kTile; idx += kThreads) {
-      const int i = idx / kTile, j = idx % kTile;
-      float s = -INFINITY;
-      if (j < nrows) {
-        float dot = 0.f;
-        for (int c = 0; c < D; ++c) dot = fmaf(qs[i][c], ks[j][c], dot);
-        s = dot * a.scale;
-      }
-      ss[i][j] = s;
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int kk = 0; kk < D / 4; ++kk) sc = mma4(ks[16 * wave + l16][4 * kk + q4], qs[l16][4 * kk + q4], sc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * wave + 4 * q4 + r;
+      ps[l16][key] = key < nrows ? sc[r] * a.scale : -INFINITY;
     }
     __syncthreads();
-    float tmax = -INFINITY;
-    for (int j = 0; j < nrows; ++j) tmax = fmaxf(tmax, ss[row][j]);
+    float x[kTile / 16], tmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kTile / 16; ++u) {
+      x[u] = ps[row][cg + 16 * u];
+      tmax = fmaxf(tmax, x[u]);
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off, 16));
     const float mnew = fmaxf(m, tmax);
     const float alpha = m == -INFINITY ? 0.f : expf(m - mnew);
-    l *= alpha;
+    float rs = 0.f;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) acc[u] *= alpha;
-    for (int j = 0; j < nrows; ++j) {
-      const float p = expf(ss[row][j] - mnew);
-      l += p;
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) acc[u] = fmaf(p, vs[j][cg + 16 * u], acc[u]);
+    for (int u = 0; u < kTile / 16; ++u) {
+      const int j = cg + 16 * u;
+      const float pv = j < nrows ? expf(x[u] - mnew) : 0.f;
+      ps[row][j] = pv;
+      rs += pv;
     }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) rs += __shfl_xor(rs, off, 16);
+    l = l * alpha + rs;
     m = mnew;
+    if (cg == 0) alpha_s[row] = alpha;
+    __syncthreads();
+    const float al = alpha_s[l16];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int dt = wave + 4 * t;
+      oacc[t] *= al;
+#pragma unroll 4
+      for (int kk = 0; kk < kTile / 4; ++kk)
+        oacc[t] = mma4(vs[4 * kk + q4][16 * dt + l16], ps[l16][4 * kk + q4], oacc[t]);
+    }
   };
 
   if (a.k_self != nullptr)
@@ -102,12 +134,20 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(AttnArgs a) {
     process(static_cast<const float*>(a.k), static_cast<const float*>(a.v), r0, n);
   });
 
-  const int64_t orow = static_cast<int64_t>(kBlock * b + row) * a.hq + h;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (cg == 0) {
+    l_s[row] = l;
+    const int64_t orow = static_cast<int64_t>(kBlock * b + row) * a.hq + h;
+    a.lse[orow] = l > 0.f ? m + logf(l) : -INFINITY;
+  }
+  __syncthreads();
+  const float lq = l_s[l16];
+  const float inv = lq > 0.f ? 1.f / lq : 0.f;
+  const int64_t orow = static_cast<int64_t>(kBlock * b + l16) * a.hq + h;
   float* O = static_cast<float*>(a.o);
 #pragma unroll
-  for (int u = 0; u < CPT; ++u) O[orow * D + cg + 16 * u] = acc[u] * inv;
-  if (cg == 0) a.lse[orow] = l > 0.f ? m + logf(l) : -INFINITY;
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) O[orow * D + 16 * (wave + 4 * t) + 4 * q4 + r] = oacc[t][r] * inv;
 }
 
 // delta[row] = sum_d dout[row][d] * o[row][d], and delta[rows + row] = lse[row] in
@@ -138,21 +178,25 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const T* __restrict__ o
 }
 
 // Query-major backward: dq_accum[i][h] += scale * sum_j dS_ij K_j over this call's keys.
+// Per 64-key tile, wave w forms S^T = K Q^T and dP^T = V dO^T for keys [16 w, 16 w + 16)
+// on the matrix cores and dS = P (dP - delta) in place; then dQ^T += K^T dS^T, each
+// wave owning D / 64 of the 16-column tiles.
 template <int D>
 __global__ __launch_bounds__(kThreads) void dq_f32_kernel(AttnArgs a, bool overwrite) {
-  constexpr int CPT = D / 16;
+  constexpr int TPW = D / 64;
   const int b = blockIdx.x, h = blockIdx.y;
   const int g = h / (a.hq / a.hkv);
   const int lo = a.sample_start[b], hi = a.anchor[b];
   const float* Q = static_cast<const float*>(a.q);
   const float* dO = static_cast<const float*>(a.dout);
-  __shared__ float qs[kBlock][D];
-  __shared__ float dos[kBlock][D];
+  __shared__ float qs[kBlock][D + 1];
+  __shared__ float dos[kBlock][D + 1];
   __shared__ float ks[kTile][D + 1];
   __shared__ float vs[kTile][D + 1];
-  __shared__ float dss[kBlock][kTile];
+  __shared__ float dss[kBlock][kTile + 1];
   __shared__ float lse_s[kBlock], del_s[kBlock];
   const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, l16 = lane % 16, q4 = lane / 16;
   for (int idx = tid; idx < kBlock * D; idx += kThreads) {
     const int i = idx / D, c = idx % D;
     const int64_t src = (static_cast<int64_t>(kBlock * b + i) * a.hq + h) * D + c;
@@ -164,39 +208,40 @@ __global__ __launch_bounds__(kThreads) void dq_f32_kernel(AttnArgs a, bool overw
     lse_s[tid] = a.lse_in[r];
     del_s[tid] = a.delta[r];
   }
-  const int row = tid / 16, cg = tid % 16;
-  float acc[CPT];
+  f32x4 acc[TPW];
 #pragma unroll
-  for (int u = 0; u < CPT; ++u) acc[u] = 0.f;
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto process = [&](const float* K, const float* V, int64_t row0, int nrows) {
     __syncthreads();
-    for (int idx = tid; idx < nrows * D; idx += kThreads) {
+    for (int idx = tid; idx < kTile * D; idx += kThreads) {
       const int j = idx / D, c = idx % D;
       const int64_t src = ((row0 + j) * a.hkv + g) * D + c;
-      ks[j][c] = K[src];
-      vs[j][c] = V[src];
+      ks[j][c] = j < nrows ? K[src] : 0.f;
+      vs[j][c] = j < nrows ? V[src] : 0.f;
     }
     __syncthreads();
-    for (int idx = tid; idx < kBlock * kTile; idx += kThreads) {
-      const int i = idx / kTile, j = idx % kTile;
-      float ds = 0.f;
-      if (j < nrows && lse_s[i] != -INFINITY) {
-        float s = 0.f, dp = 0.f;
-        for (int c = 0; c < D; ++c) {
-          s = fmaf(qs[i][c], ks[j][c], s);
-          dp = fmaf(dos[i][c], vs[j][c], dp);
-        }
-        const float p = expf(s * a.scale - lse_s[i]);
-        ds = p * (dp - del_s[i]);
-      }
-      dss[i][j] = ds;
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int kk = 0; kk < D / 4; ++kk) {
+      sc = mma4(ks[16 * wave + l16][4 * kk + q4], qs[l16][4 * kk + q4], sc);
+      dp = mma4(vs[16 * wave + l16][4 * kk + q4], dos[l16][4 * kk + q4], dp);
     }
-    __syncthreads();
-    for (int j = 0; j < nrows; ++j) {
-      const float ds = dss[row][j];
+    const float lq = lse_s[l16], dq_ = del_s[l16];
 #pragma unroll
-      for (int u = 0; u < CPT; ++u) acc[u] = fmaf(ds, ks[j][cg + 16 * u], acc[u]);
+    for (int r = 0; r < 4; ++r) {
+      const int key = 16 * wave + 4 * q4 + r;
+      float ds = 0.f;
+      if (key < nrows && lq != -INFINITY) ds = expf(sc[r] * a.scale - lq) * (dp[r] - dq_);
+      dss[l16][key] = ds;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int dt = wave + 4 * t;
+#pragma unroll 4
+      for (int kk = 0; kk < kTile / 4; ++kk)
+        acc[t] = mma4(ks[4 * kk + q4][16 * dt + l16], dss[l16][4 * kk + q4], acc[t]);
     }
   };
 
@@ -206,23 +251,29 @@ __global__ __launch_bounds__(kThreads) void dq_f32_kernel(AttnArgs a, bool overw
   for_each_ctx_tile(a, lo, hi, [&](int64_t r0, int n) {
     process(static_cast<const float*>(a.k), static_cast<const float*>(a.v), r0, n);
   });
-  const int64_t orow = static_cast<int64_t>(kBlock * b + row) * a.hq + h;
+  const int64_t orow = static_cast<int64_t>(kBlock * b + l16) * a.hq + h;
 #pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    float* dst = a.dq + orow * D + cg + 16 * u;
-    *dst = overwrite ? a.scale * acc[u] : *dst + a.scale * acc[u];
-  }
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* dst = a.dq + orow * D + 16 * (wave + 4 * t) + 4 * q4 + r;
+      *dst = overwrite ? a.scale * acc[t][r] : *dst + a.scale * acc[t][r];
+    }
 }
 
 // Key-major backward over tiles of 16 key rows: the local context rows, then (when
 // k_self is given) one tile per block of own-block rows.  dK, dV are overwritten.
+// Per (block, head) that may read the tile: wave 0 forms S^T = K Q^T and dP^T = V dO^T
+// (16 keys x 16 queries) on the matrix cores and writes P and dS; then every wave adds
+// dV^T += dO^T P and dK^T += Q^T dS for its D / 64 of the 16-column tiles.
 template <int D>
 __global__ __launch_bounds__(kThreads) void dkdv_f32_kernel(AttnArgs a, int n_ctx_tiles) {
-  constexpr int CPT = D / 16;
+  constexpr int TPW = D / 64;
   const int kt = blockIdx.x, g = blockIdx.y;
   const int grp = a.hq / a.hkv;
   const bool self_tile = kt >= n_ctx_tiles;
   const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64, l16 = lane % 16, q4 = lane / 16;
   const float* K = static_cast<const float*>(self_tile ? a.k_self : a.k);
   const float* V = static_cast<const float*>(self_tile ? a.v_self : a.v);
   const float* Q = static_cast<const float*>(a.q);
@@ -231,8 +282,8 @@ __global__ __launch_bounds__(kThreads) void dkdv_f32_kernel(AttnArgs a, int n_ct
   __shared__ float vs[kBlock][D + 1];
   __shared__ float qs[kBlock][D + 1];
   __shared__ float dos[kBlock][D + 1];
-  __shared__ float ps[kBlock][kBlock + 1];
-  __shared__ float dss[kBlock][kBlock + 1];
+  __shared__ float ps[kBlock][kBlock + 1];   // [query][key]
+  __shared__ float dss[kBlock][kBlock + 1];  // [query][key]
   __shared__ int gpos[kBlock];
   __shared__ float lse_s[kBlock], del_s[kBlock];
   const int64_t row0 = self_tile ? static_cast<int64_t>(kt - n_ctx_tiles) * kBlock
@@ -267,10 +318,9 @@ __global__ __launch_bounds__(kThreads) void dkdv_f32_kernel(AttnArgs a, int n_ct
     vs[j][c] = vv;
   }
   __syncthreads();
-  const int key = tid / 16, cg = tid % 16;
-  float dk[CPT], dv[CPT];
+  f32x4 dk[TPW], dv[TPW];
 #pragma unroll
-  for (int u = 0; u < CPT; ++u) dk[u] = dv[u] = 0.f;
+  for (int t = 0; t < TPW; ++t) dk[t] = dv[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int b_begin = self_tile ? kt - n_ctx_tiles : 0;
   const int b_end = self_tile ? b_begin + 1 : a.n_blk;
   for (int b = b_begin; b < b_end; ++b) {
@@ -293,43 +343,53 @@ __global__ __launch_bounds__(kThreads) void dkdv_f32_kernel(AttnArgs a, int n_ct
         del_s[tid] = a.delta[r];
       }
       __syncthreads();
-      {
-        const int i = tid / 16, j = tid % 16;
-        const bool allowed = j < nrows && (self_tile || (gpos[j] >= lo && gpos[j] < hi)) &&
-                             lse_s[i] != -INFINITY;
-        float p = 0.f, ds = 0.f;
-        if (allowed) {
-          float s = 0.f, dp = 0.f;
-          for (int c = 0; c < D; ++c) {
-            s = fmaf(qs[i][c], ks[j][c], s);
-            dp = fmaf(dos[i][c], vs[j][c], dp);
-          }
-          p = expf(s * a.scale - lse_s[i]);
-          ds = p * (dp - del_s[i]);
+      if (wave == 0) {
+        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int kk = 0; kk < D / 4; ++kk) {
+          sc = mma4(ks[l16][4 * kk + q4], qs[l16][4 * kk + q4], sc);
+          dp = mma4(vs[l16][4 * kk + q4], dos[l16][4 * kk + q4], dp);
         }
-        ps[i][j] = p;
-        dss[i][j] = ds;
+        // lane: keys 4 q4 + r of the tile, query l16
+        const float lq = lse_s[l16], dq_ = del_s[l16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 4 * q4 + r;
+          const bool allowed = j < nrows && (self_tile || (gpos[j] >= lo && gpos[j] < hi)) && lq != -INFINITY;
+          float pv = 0.f, ds = 0.f;
+          if (allowed) {
+            pv = expf(sc[r] * a.scale - lq);
+            ds = pv * (dp[r] - dq_);
+          }
+          ps[l16][j] = pv;
+          dss[l16][j] = ds;
+        }
       }
       __syncthreads();
-      for (int i = 0; i < kBlock; ++i) {
-        const float p = ps[i][key], ds = dss[i][key];
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-          dv[u] = fmaf(p, dos[i][cg + 16 * u], dv[u]);
-          dk[u] = fmaf(ds, qs[i][cg + 16 * u], dk[u]);
+      for (int t = 0; t < TPW; ++t) {
+        const int dt = wave + 4 * t;
+#pragma unroll
+        for (int kk = 0; kk < kBlock / 4; ++kk) {
+          dv[t] = mma4(dos[4 * kk + q4][16 * dt + l16], ps[4 * kk + q4][l16], dv[t]);
+          dk[t] = mma4(qs[4 * kk + q4][16 * dt + l16], dss[4 * kk + q4][l16], dk[t]);
         }
       }
     }
   }
-  if (key < nrows) {
+  // lane holds column l16 (a key) of the dcol rows 16 dt + 4 q4 + r
+  if (l16 < nrows) {
     float* dK = static_cast<float*>(self_tile ? a.dk_self : a.dk);
     float* dV = static_cast<float*>(self_tile ? a.dv_self : a.dv);
-    const int64_t dst = ((row0 + key) * a.hkv + g) * D;
+    const int64_t dst = ((row0 + l16) * a.hkv + g) * D;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      dK[dst + cg + 16 * u] = a.scale * dk[u];
-      dV[dst + cg + 16 * u] = dv[u];
-    }
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 16 * (wave + 4 * t) + 4 * q4 + r;
+        dK[dst + c] = a.scale * dk[t][r];
+        dV[dst + c] = dv[t][r];
+      }
   }
 }
 
