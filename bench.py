@@ -5,8 +5,9 @@ One step is one pass of the whole path over the 8192-query x 65536-token packed
 context (Hq = 32, Hkv = 8, head_dim = 128, bf16), split into 64 chunks of 1024
 tokens and planned onto 8 virtual devices ("bins"):
 
-  1. chunk_cost   realised cost of each chunk (GPU, int64), copied to the host
-  2. lpt_assign   longest-processing-time-first plan with equal chunk counts (host)
+  1. chunk_cost   realised cost of each chunk (GPU, int64)
+  2. lpt_plan     longest-processing-time-first plan with equal chunk counts (GPU; the
+                  same plan as the host lpt_assign, so nothing returns to the host)
   3. per bin: context_gather of its chunks of K and V into its local buffer, then
      sparse_xattn_fwd (the own-block term on bin 0): partial O, lse; the bins
      alternate between two streams, so their gathers and forwards overlap
@@ -18,11 +19,11 @@ Throughput is useful attention FLOP/s: 4*d*Hq FLOP per allowed (query, key) pair
 for the forward and 10*d*Hq for the backward, over the allowed pairs only
 (context pairs from the cost kernel plus 16 own-block pairs per query).
 
-Prints one JSON line.  The timed steps carry HIP events only around the dominant
-phase (one pair per step around its 8 launches): recording an event costs GPU time,
-so events around every launch would slow the step they measure.  The per-phase
-breakdown comes from the warm-up steps, which carry events around every phase.  The
-CPU oracle is timed on a bounded sample of blocks of the same workload.
+Prints one JSON line.  The timed steps carry no HIP events (recording one costs GPU
+time); the per-phase breakdown comes from the warm-up steps, which carry events
+around every phase, and the dominant phase's roofline from its calls run alone after
+the timed steps.  The CPU oracle is timed on a bounded sample of blocks of the same
+workload.
 
 `--combine P` times the P-way combine of the 8192-query view instead (every partial
 live, and the empty pattern of the 524288-token workload on P bins; one JSON line).
@@ -159,10 +160,12 @@ def build_problem(torch, seed, split=False, inputs=None, bwd_schedule="overlap")
     P["delta"] = torch.empty((2, n_q, hq), dtype=f32, device="cuda")
     P["dq"] = torch.empty((n_q, hq, d), dtype=f32, device="cuda")
     P["cost"] = torch.empty((w.n_chunk,), dtype=torch.int64, device="cuda")
-    # the plan's host side in allocated pinned memory: one D2H of the costs and one
-    # H2D of the packed plan per step, neither through a staging copy
-    P["cost_h"] = torch.empty((w.n_chunk,), dtype=torch.int64, pin_memory=True)
-    P["plan_h"] = torch.empty((2, nb, per_bin), dtype=torch.int32, pin_memory=True)
+    # the device plan: every chunk's bin, every bin's load, and each bin's chunk list
+    # (starts, lengths), which the gathers and attention calls of that bin read
+    P["chunk_gs_d"] = torch.as_tensor(gs).cuda()
+    P["chunk_gl_d"] = torch.as_tensor(gl).cuda()
+    P["bin_of_d"] = torch.empty((w.n_chunk,), dtype=torch.int32, device="cuda")
+    P["load_d"] = torch.empty((nb,), dtype=torch.int64, device="cuda")
     P["plan"] = torch.empty((2, nb, per_bin), dtype=torch.int32, device="cuda")
     P["plan_gs"], P["plan_gl"] = P["plan"][0], P["plan"][1]
     P["per_bin"], P["n_loc"] = per_bin, n_loc
@@ -184,7 +187,6 @@ def build_problem(torch, seed, split=False, inputs=None, bwd_schedule="overlap")
         P["metas"].append(m)
     P["live_rows"] = {}   # live partial rows of the combine, per plan
     P["ev_fork"] = torch.cuda.Event()
-    P["ev_cost"] = torch.cuda.Event()
     P["ev_fork_dq"] = torch.cuda.Event()
     P["ev_join_dq"] = torch.cuda.Event()
     P["ev_join"] = torch.cuda.Event()
@@ -215,60 +217,69 @@ def build_problem(torch, seed, split=False, inputs=None, bwd_schedule="overlap")
     fws = int(lib.sparse_xattn_fwd_split_workspace_bytes(w.n_anchor, hq, hkv, d) if split
               else lib.sparse_xattn_fwd_workspace_bytes(w.n_anchor, hq, hkv))
     P["fwd_ws"] = [torch.empty((max(fws, 256),), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    # The same plan on the host, once: the GPU costs copied back and the host LPT.  The
+    # step plans on the device; these host values only size the timers' work and the
+    # reported fields (the metadata, hence the plan, is the same every step), and
+    # check_device_plan() compares the device's plan with them after the timed steps.
+    sxattn.chunk_cost(P["anchor"], P["start"], w.n_ctx, w.chunk_size, out=P["cost"])
+    cost_np = P["cost"].cpu().numpy()
+    bins, load = sxattn.lpt_assign(cost_np, nb)
+    bins_np = bins.numpy()
+    order = np.argsort(bins_np, kind="stable").reshape(nb, per_bin)   # chunks of each bin
+    P["host_plan"] = (bins_np, load.numpy(), cost_np, order)
     return P
 
 
 def plan(torch, P, T):
-    """Steps 1 and 2 of the hot path: the GPU cost of every chunk, copied to the host,
-    the host LPT plan, and its upload into the device plan buffers that every later
-    launch reads.  Returns (bins, load, cost, chunks of each bin) on the host."""
+    """Steps 1 and 2 of the hot path, on the device: the cost of every chunk, then the
+    LPT plan into the plan buffers that every later launch reads.  Nothing returns to
+    the host, so the step is enqueued without waiting for the GPU."""
     from block_sparse_cross_anchor_amd import sxattn
 
     w = P["w"]
-    nb, per_bin = w.n_bin, P["per_bin"]
     T.run("chunk_cost", 8 * w.n_anchor + 8 * w.n_chunk,
           lambda: sxattn.chunk_cost(P["anchor"], P["start"], w.n_ctx, w.chunk_size, out=P["cost"]))
-    # device -> host; the host polls the copy's event instead of blocking in the copy,
-    # so it resumes as soon as the costs have landed
-    P["cost_h"].copy_(P["cost"], non_blocking=True)
-    P["ev_cost"].record()
-    while not P["ev_cost"].query():
-        pass
-    cost = P["cost_h"]
-    bins, load = sxattn.lpt_assign(cost, nb)                # host planner
-    bins_np = bins.numpy()
-    order = np.argsort(bins_np, kind="stable").reshape(nb, per_bin)   # chunks of each bin
-    plan_h = P["plan_h"].numpy()
-    plan_h[0] = P["chunk_gs"][order]
-    plan_h[1] = P["chunk_gl"][order]
-    # the host buffer is next written after the next step's cost copy, which waits
-    # for this copy
-    P["plan"].copy_(P["plan_h"], non_blocking=True)
-    return bins_np, load, cost.numpy(), order
+    T.run("lpt_plan", 8 * w.n_chunk + 8 * w.n_chunk + 8 * w.n_bin + 8 * w.n_chunk,
+          lambda: sxattn.lpt_plan(P["cost"], P["chunk_gs_d"], P["chunk_gl_d"], w.n_bin,
+                                  bin_of=P["bin_of_d"], load=P["load_d"], plan=P["plan"]))
 
 
 def step(torch, P, T):
-    """One pass of the hot path; returns the host-side plan (bins, load, cost) and the
-    allowed pairs of each bin.  With a captured graph (P["graph"]) the launches after
-    the plan upload are one replay of it."""
-    bins_np, load, cost_np, order = plan(torch, P, T)
+    """One pass of the hot path; returns the plan (bins, load, cost) and the allowed
+    pairs of each bin, from the host copy of the plan.  With a captured graph
+    (P["graph"]) the whole step is one replay of it."""
+    bins_np, load, cost_np, order = P["host_plan"]
     if P.get("graph") is not None:
         P["graph"].replay()
         bin_pairs = [int(cost_np[order[b]].sum()) for b in range(P["w"].n_bin)]
     else:
+        plan(torch, P, T)
         bin_pairs = post_plan(torch, P, T, bins_np, cost_np, order)
-    return bins_np, load.numpy(), cost_np, bin_pairs
+    return bins_np, load, cost_np, bin_pairs
+
+
+def check_device_plan(torch, P):
+    """The device plan of the last step equals the host plan (bins, loads, lists)."""
+    bins_np, load, _, order = P["host_plan"]
+    torch.cuda.synchronize()
+    ok = (np.array_equal(P["bin_of_d"].cpu().numpy(), bins_np)
+          and np.array_equal(P["load_d"].cpu().numpy(), load)
+          and np.array_equal(P["plan"][0].cpu().numpy(), P["chunk_gs"][order])
+          and np.array_equal(P["plan"][1].cpu().numpy(), P["chunk_gl"][order]))
+    if not ok:
+        raise RuntimeError("the device LPT plan differs from the host plan")
 
 
 def capture_graph(torch, P):
-    """Capture the launches of a step after its plan upload (gathers, forwards,
-    combine, delta, dQ and dK/dV phases on both streams) into one HIP graph.  They
-    read the plan from the device buffers every replay rewrites, so one capture serves
-    every step; the capture itself runs nothing."""
-    bins_np, _, cost_np, order = plan(torch, P, _NoTimer())
+    """Capture a whole step (costs, device plan, gathers, forwards, combine, delta,
+    dQ and dK/dV phases on both streams) into one HIP graph.  The plan is computed on
+    the device inside it, so one capture serves every step; the capture itself runs
+    nothing."""
+    bins_np, _, cost_np, order = P["host_plan"]
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
+        plan(torch, P, _NoTimer())
         post_plan(torch, P, _NoTimer(), bins_np, cost_np, order)
     torch.cuda.synchronize()
     P["graph"] = g
@@ -919,6 +930,7 @@ def main():
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     gc.enable()
+    check_device_plan(torch, P)
     ms_step = el * 1e3 / args.steps
     ctx_pairs = int(cost.sum())
     pairs = ctx_pairs + 16 * w.n_q

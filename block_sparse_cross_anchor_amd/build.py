@@ -23,7 +23,7 @@ OUT = os.path.join(HERE, "libsxattn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "cost.hip", "combine.hip", "gather.hip", "order.hip", "attn_f32.hip",
+SOURCES = ["api.hip", "cost.hip", "combine.hip", "gather.hip", "order.hip", "plan.hip", "attn_f32.hip",
            "attn_fwd.hip", "attn_bwd.hip",
            "lpt.cpp"]
 

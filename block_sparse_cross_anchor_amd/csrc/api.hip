@@ -357,4 +357,21 @@ int lpt_assign(const int64_t* cost, int32_t n_chunk, int32_t n_bin, int32_t* bin
   return ok();
 }
 
+int lpt_plan(const int64_t* cost, const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
+             int32_t n_bin, int32_t* bin_of_chunk, int64_t* bin_load, int32_t* plan_gstart, int32_t* plan_len,
+             void* stream) {
+  if (n_bin <= 0) return fail(SXA_EINVAL, "n_bin must be > 0 (got %d)", n_bin);
+  if (n_chunk <= 0 || n_chunk % n_bin != 0)
+    return fail(SXA_EINVAL, "n_chunk (%d) must be a positive multiple of n_bin (%d)", n_chunk, n_bin);
+  if (n_chunk > sxa::kMaxPlanChunks || n_bin > sxa::kMaxPlanBins)
+    return fail(SXA_EUNSUPPORTED, "lpt_plan takes at most %d chunks and %d bins (got %d, %d; use lpt_assign)",
+                sxa::kMaxPlanChunks, sxa::kMaxPlanBins, n_chunk, n_bin);
+  if (cost == nullptr || chunk_gstart == nullptr || chunk_len == nullptr || bin_of_chunk == nullptr ||
+      bin_load == nullptr || plan_gstart == nullptr || plan_len == nullptr)
+    return fail(SXA_EINVAL, "lpt_plan: pointers must not be NULL");
+  return hip_status(sxa::launch_lpt_plan(cost, n_chunk, n_bin, chunk_gstart, chunk_len, bin_of_chunk, bin_load,
+                                         plan_gstart, plan_len, static_cast<hipStream_t>(stream)),
+                    "lpt_plan launch");
+}
+
 }  // extern "C"

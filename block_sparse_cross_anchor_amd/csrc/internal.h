@@ -102,5 +102,11 @@ hipError_t launch_context_gather(const void* src, int64_t row_bytes, const int32
                                  void* dst, hipStream_t s);
 hipError_t launch_chunk_cost(const int32_t* anchor, const int32_t* sample_start, int32_t n_blk,
                              int32_t n_ctx, int32_t chunk_size, int64_t* cost, hipStream_t s);
+// The device LPT plan (one workgroup; the arrays live in LDS up to these sizes).
+constexpr int kMaxPlanChunks = 4096;
+constexpr int kMaxPlanBins = 1024;
+hipError_t launch_lpt_plan(const int64_t* cost, int32_t n_chunk, int32_t n_bin, const int32_t* chunk_gstart,
+                           const int32_t* chunk_len, int32_t* bin_of, int64_t* bin_load, int32_t* plan_gstart,
+                           int32_t* plan_len, hipStream_t s);
 
 }  // namespace sxa

@@ -25,7 +25,7 @@ BLOCK = 16
 EXPORTS = ("sparse_xattn_fwd", "sparse_xattn_fwd_noalloc", "sparse_xattn_fwd_workspace_bytes",
            "sparse_xattn_fwd_split_workspace_bytes", "sparse_xattn_bwd",
            "sparse_xattn_bwd_workspace_bytes", "sparse_xattn_bwd_split_workspace_bytes",
-           "lse_combine", "chunk_cost", "lpt_assign", "context_gather", "sxa_last_error")
+           "lse_combine", "chunk_cost", "lpt_assign", "lpt_plan", "context_gather", "sxa_last_error")
 
 _lib = None
 
@@ -69,6 +69,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.chunk_cost.restype = ctypes.c_int
     lib.lpt_assign.argtypes = [P, I32, I32, P, P]
     lib.lpt_assign.restype = ctypes.c_int
+    lib.lpt_plan.argtypes = [P, P, P, I32, I32, P, P, P, P, P]
+    lib.lpt_plan.restype = ctypes.c_int
     lib.context_gather.argtypes = [P, I64, P, P, I32, I64, P, P]
     lib.context_gather.restype = ctypes.c_int
     lib.sxa_last_error.argtypes = []
@@ -329,6 +331,29 @@ def context_gather(src, chunk_gstart, chunk_len, n_rows: int, out=None):
     _check(lib.context_gather(_ptr(src), row_bytes, _ptr(chunk_gstart), _ptr(chunk_len),
                               int(chunk_gstart.numel()), int(n_rows), _ptr(out), _stream()))
     return out
+
+
+def lpt_plan(cost, chunk_gstart, chunk_len, n_bin: int, bin_of=None, load=None, plan=None):
+    """Device LPT plan, asynchronous on the current stream.  cost: int64, chunk_gstart
+    and chunk_len: int32 CUDA tensors of n_chunk entries.  Returns (bin_of_chunk int32
+    [n_chunk], bin_load int64 [n_bin], plan int32 [2, n_bin, n_chunk / n_bin]), plan[0]
+    and plan[1] holding each bin's chunk starts and lengths in increasing chunk index."""
+    n = int(cost.numel())
+    nb = int(n_bin)
+    for t, name, dt in ((cost, "cost", torch.int64), (chunk_gstart, "chunk_gstart", torch.int32),
+                        (chunk_len, "chunk_len", torch.int32)):
+        _need(t, name, (n,), dt)
+    per = n // nb if nb > 0 else 0
+    dev = cost.device
+    bin_of = torch.empty((n,), dtype=torch.int32, device=dev) if bin_of is None else bin_of
+    load = torch.empty((max(nb, 0),), dtype=torch.int64, device=dev) if load is None else load
+    plan = torch.empty((2, max(nb, 0), per), dtype=torch.int32, device=dev) if plan is None else plan
+    _need(bin_of, "bin_of", (n,), torch.int32)
+    _need(load, "load", (max(nb, 0),), torch.int64)
+    _need(plan, "plan", (2, max(nb, 0), per), torch.int32)
+    _check(load_library().lpt_plan(_ptr(cost), _ptr(chunk_gstart), _ptr(chunk_len), n, nb, _ptr(bin_of),
+                                   _ptr(load), _ptr(plan[0]), _ptr(plan[1]), _stream()))
+    return bin_of, load, plan
 
 
 def lpt_assign(cost, n_bin: int):

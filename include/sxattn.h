@@ -241,6 +241,24 @@ int lpt_assign(const int64_t* cost, int32_t n_chunk, int32_t n_bin, int32_t* bin
                int64_t* bin_load);
 
 /*
+ * The same plan on the device ("Balance actual attention work"), so that a step that
+ * prices its chunks on the GPU plans them without a round trip through the host.
+ * DEVICE pointers, asynchronous on `stream`; one workgroup.
+ *   cost[n_chunk] int64 >= 0 (not validated on the device); chunk_gstart[n_chunk],
+ *   chunk_len[n_chunk] int32: each chunk's global start and length.
+ *   bin_of_chunk[n_chunk] and bin_load[n_bin] are overwritten with exactly what
+ *   lpt_assign returns for the same costs.  plan_gstart and plan_len
+ *   [n_bin][n_chunk / n_bin] are overwritten with each bin's chunks (their global
+ *   starts and lengths) in increasing chunk index: the chunk lists that
+ *   context_gather and the attention calls of that bin take.
+ *   n_chunk must be a positive multiple of n_bin (SXA_EINVAL); at most 4096 chunks
+ *   and 1024 bins (SXA_EUNSUPPORTED beyond: use lpt_assign).
+ */
+int lpt_plan(const int64_t* cost, const int32_t* chunk_gstart, const int32_t* chunk_len, int32_t n_chunk,
+             int32_t n_bin, int32_t* bin_of_chunk, int64_t* bin_load, int32_t* plan_gstart, int32_t* plan_len,
+             void* stream);
+
+/*
  * Context redistribution: copy the rows of the listed chunks of a packed context
  * tensor back to back into a device's local buffer ("Balance actual attention
  * work": after planning, context chunks are moved once per step to the device

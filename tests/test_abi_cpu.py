@@ -53,6 +53,20 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     bins = (ctypes.c_int32 * 3)()
     load = (ctypes.c_int64 * 2)()
     assert lib.lpt_assign(cost, 3, 2, bins, load) == sxattn.SXA_EINVAL
+    # device LPT: counts not divisible, no bin, beyond its one-workgroup sizes, NULL
+    # pointers (all rejected before anything is launched)
+    fake = ctypes.c_void_p(16)
+    plan_args = [fake] * 3 + [3, 2] + [fake] * 4 + [null]
+    assert lib.lpt_plan(*plan_args) == sxattn.SXA_EINVAL
+    plan_args[3], plan_args[4] = 4, 0
+    assert lib.lpt_plan(*plan_args) == sxattn.SXA_EINVAL
+    plan_args[3], plan_args[4] = 8192, 8
+    assert lib.lpt_plan(*plan_args) == sxattn.SXA_EUNSUPPORTED
+    assert b"4096" in lib.sxa_last_error()
+    plan_args[3], plan_args[4] = 4096, 2048
+    assert lib.lpt_plan(*plan_args) == sxattn.SXA_EUNSUPPORTED
+    plan_args[3], plan_args[4], plan_args[5] = 64, 8, null
+    assert lib.lpt_plan(*plan_args) == sxattn.SXA_EINVAL
     # attention: head_dim 96 unsupported, hq not a multiple of hkv, bad scale
     args = [null, null, null, 1, 1, 16, 4, 2, 96, 0.1, null, null, null, null, 0, 0, null, null,
             null, 1, null, null, 0, null]
