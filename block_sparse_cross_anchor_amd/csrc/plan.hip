@@ -6,9 +6,11 @@
 // The same assignment as the host planner (lpt.cpp), computed by one workgroup from
 // the device-resident costs, so that a step needs no round trip through the host:
 //   1. rank the chunks by (cost descending, index ascending), in parallel;
-//   2. visit them in rank order in one wave, whose lanes hold the bins' loads and
-//      counts: each chunk goes to the bin with the least (load, index) among those
-//      with fewer than n_chunk / n_bin chunks (a wave-wide arg-min);
+//   2. visit them in rank order: each chunk goes to the bin with the least (load,
+//      index) among those with fewer than n_chunk / n_bin chunks.  Up to kScanBins
+//      bins one thread holds them in registers (no memory access or cross-lane step on
+//      the chain from one chunk to the next); beyond, one wave's lanes hold the bins
+//      and take a wave-wide arg-min;
 //   3. write each bin's chunk list in increasing chunk index (the order a stable sort
 //      of the chunks by bin gives), with the chunks' global starts and lengths.
 #include "internal.h"
@@ -17,6 +19,42 @@ namespace sxa {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kScanBins = 32;  // up to this many bins one thread scans them
+
+// The greedy visit for up to NB bins in one thread, the bins' loads and counts in
+// registers (bins past n_bin start full, so they are never chosen): a chunk costs one
+// unrolled arg-min and one unrolled charge, with no memory access on the chain.
+template <int NB>
+__device__ __forceinline__ void greedy_scan(int n, int n_bin, int cap, const long long* c_sorted,
+                                            const int* ord, int* bin_s, long long* load_s) {
+  long long ld[NB];
+  int ct[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    ld[b] = 0;
+    ct[b] = b < n_bin ? 0 : cap;
+  }
+  for (int k = 0; k < n; ++k) {
+    long long bl = 0x7fffffffffffffffLL;
+    int bb = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {  // first least: ties go to the lower index
+      const bool better = ct[b] < cap && ld[b] < bl;
+      bl = better ? ld[b] : bl;
+      bb = better ? b : bb;
+    }
+    const long long c = c_sorted[k];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      ld[b] += b == bb ? c : 0;
+      ct[b] += b == bb ? 1 : 0;
+    }
+    bin_s[ord[k]] = bb;
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    if (b < n_bin) load_s[b] = ld[b];
+}
 
 __global__ __launch_bounds__(kPlanThreads) void lpt_plan_kernel(const int64_t* __restrict__ cost, int32_t n,
                                                                 int32_t n_bin, const int32_t* __restrict__ chunk_gstart,
@@ -25,6 +63,7 @@ __global__ __launch_bounds__(kPlanThreads) void lpt_plan_kernel(const int64_t* _
                                                                 int32_t* __restrict__ plan_gstart,
                                                                 int32_t* __restrict__ plan_len) {
   __shared__ long long c_s[kMaxPlanChunks];
+  __shared__ long long c_sorted[kMaxPlanChunks];  // costs in visiting order
   __shared__ int ord[kMaxPlanChunks];
   __shared__ int bin_s[kMaxPlanChunks];
   __shared__ long long load_s[kMaxPlanBins];
@@ -45,9 +84,16 @@ __global__ __launch_bounds__(kPlanThreads) void lpt_plan_kernel(const int64_t* _
       rank += (cj > ci) | ((cj == ci) & (j < i));
     }
     ord[rank] = i;
+    c_sorted[rank] = ci;
   }
   __syncthreads();
-  if (tid < 64) {
+  if (n_bin <= kScanBins) {
+    if (tid == 0) {
+      if (n_bin <= 8) greedy_scan<8>(n, n_bin, cap, c_sorted, ord, bin_s, load_s);
+      else if (n_bin <= 16) greedy_scan<16>(n, n_bin, cap, c_sorted, ord, bin_s, load_s);
+      else greedy_scan<kScanBins>(n, n_bin, cap, c_sorted, ord, bin_s, load_s);
+    }
+  } else if (tid < 64) {
     const int lane = tid;
     for (int k = 0; k < n; ++k) {
       const int c = ord[k];

@@ -12,6 +12,8 @@
 // Writes:
 // DIR/cost.bin   int64 [ceil(n_ctx / chunk_size)]   chunk_cost over the whole context
 // DIR/bins.bin   int32, DIR/load.bin int64          lpt_assign of those costs onto n_bin
+// DIR/dbins.bin, dload.bin, dplan_gs.bin, dplan_gl.bin  lpt_plan of the device costs (its
+//                bins and loads, and each bin's chunk starts and lengths [n_bin][n_all / n_bin])
 // DIR/o.bin      bf16 bits, DIR/lse.bin float32     sparse_xattn_fwd over every listed chunk
 //                                                   plus the own-block term
 // DIR/o2.bin, DIR/lse2.bin                          the same from two calls (first half of the
@@ -123,6 +125,22 @@ int run(const std::string& dir) {
   write_file(dir + "/cost.bin", cost);
   write_file(dir + "/bins.bin", bins);
   write_file(dir + "/load.bin", load);
+  // the same plan on the device, from the device costs, with each bin's chunk list
+  std::vector<int32_t> all_gs(n_all), all_gl(n_all);
+  for (int64_t c = 0; c < n_all; ++c) {
+    all_gs[c] = static_cast<int32_t>(c * chunk_size);
+    all_gl[c] = static_cast<int32_t>(std::min<int64_t>(chunk_size, n_ctx - c * chunk_size));
+  }
+  Dev<int32_t> d_all_gs(all_gs), d_all_gl(all_gl), d_bins(n_all), d_plan_gs(n_all), d_plan_gl(n_all);
+  Dev<int64_t> d_load(n_bin);
+  sxa_check(lpt_plan(d_cost.p, d_all_gs.p, d_all_gl.p, static_cast<int32_t>(n_all), static_cast<int32_t>(n_bin),
+                     d_bins.p, d_load.p, d_plan_gs.p, d_plan_gl.p, s),
+            "lpt_plan");
+  hip_check(hipStreamSynchronize(s), "sync");
+  write_file(dir + "/dbins.bin", d_bins.host());
+  write_file(dir + "/dload.bin", d_load.host());
+  write_file(dir + "/dplan_gs.bin", d_plan_gs.host());
+  write_file(dir + "/dplan_gl.bin", d_plan_gl.host());
 
   // forward over every listed chunk, with the own-block term
   const int64_t rows = n_q * hq;

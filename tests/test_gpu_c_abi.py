@@ -62,6 +62,15 @@ def test_c_driver_matches_oracle(tmp_path, seed, order):
     want_bins, want_load = oracle.lpt_assign(want_cost, n_bin)
     assert np.fromfile(d / "bins.bin", np.int32).tolist() == want_bins
     assert np.fromfile(d / "load.bin", np.int64).tolist() == want_load
+    # the device planner, from the device costs: the same plan, and each bin's chunks
+    assert np.fromfile(d / "dbins.bin", np.int32).tolist() == want_bins
+    assert np.fromfile(d / "dload.bin", np.int64).tolist() == want_load
+    n_all = len(want_cost)
+    all_gs = np.arange(n_all, dtype=np.int64) * w.chunk_size
+    all_gl = np.minimum(w.chunk_size, w.n_ctx - all_gs)
+    order = np.argsort(np.asarray(want_bins), kind="stable")
+    np.testing.assert_array_equal(np.fromfile(d / "dplan_gs.bin", np.int32), all_gs[order])
+    np.testing.assert_array_equal(np.fromfile(d / "dplan_gl.bin", np.int32), all_gl[order])
 
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     ro, rl = oracle.sparse_xattn_fwd(inp.q.f64, inp.k.f64, inp.v.f64, meta.anchor,
