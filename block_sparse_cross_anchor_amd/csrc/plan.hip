@@ -34,6 +34,7 @@ __device__ __forceinline__ void greedy_scan(int n, int n_bin, int cap, const lon
     ld[b] = 0;
     ct[b] = b < n_bin ? 0 : cap;
   }
+#pragma unroll 4
   for (int k = 0; k < n; ++k) {
     long long bl = 0x7fffffffffffffffLL;
     int bb = 0;
@@ -79,6 +80,7 @@ __global__ __launch_bounds__(kPlanThreads) void lpt_plan_kernel(const int64_t* _
   for (int i = tid; i < n; i += kPlanThreads) {
     const long long ci = c_s[i];
     int rank = 0;
+#pragma unroll 8
     for (int j = 0; j < n; ++j) {
       const long long cj = c_s[j];
       rank += (cj > ci) | ((cj == ci) & (j < i));
@@ -128,6 +130,7 @@ __global__ __launch_bounds__(kPlanThreads) void lpt_plan_kernel(const int64_t* _
   for (int i = tid; i < n; i += kPlanThreads) {
     const int b = bin_s[i];
     int pos = 0;
+#pragma unroll 8
     for (int j = 0; j < i; ++j) pos += bin_s[j] == b;
     bin_of[i] = b;
     plan_gstart[static_cast<int64_t>(b) * cap + pos] = chunk_gstart[i];
