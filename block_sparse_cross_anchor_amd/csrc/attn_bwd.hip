@@ -309,32 +309,34 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kDqWaves, 64 * kDqWav
     }
 }
 
-// Merge of a split row group's dQ pieces, one workgroup per (split group, kv head,
-// run of 256 / (d / 4) rows), d / 4 lanes per row: dq = (overwrite ? 0 : dq) + the
-// pieces' sums in piece order.  Workgroups of unused split-group entries return.
+// Merge of the split row groups' dQ pieces, one workgroup per (kv head, run of
+// 256 / (d / 4) rows) looping over the split groups until the first unused entry,
+// d / 4 lanes per row: dq = (overwrite ? 0 : dq) + the pieces' sums in piece order.
+// A small fixed grid, as for the forward's merge.
 template <int D>
 __global__ __launch_bounds__(256) void dq_merge_kernel(RowSplit sp, float* dq, int32_t n_blk, int32_t hq, int32_t hkv,
                                                        int32_t overwrite) {
   constexpr int LPR = D / 4;                 // lanes per row, 4 values each
   constexpr int RPW = 256 / LPR;             // rows per workgroup
-  constexpr int RUNS = kRowsPerGroup / RPW;  // workgroups per (split group, kv head)
   const int g = blockIdx.x % hkv;
-  const int run = (blockIdx.x / hkv) % RUNS;
-  const int4 jb = sp.groups[blockIdx.x / hkv / RUNS];
-  if (jb.x < 0) return;
+  const int run = blockIdx.x / hkv;  // < kRowsPerGroup / RPW
   const int grp = hq / hkv;
   const int64_t R = static_cast<int64_t>(n_blk) * kBlock * grp;
   const int sub = threadIdx.x % LPR;
   const int lr = run * RPW + threadIdx.x / LPR;
-  const int64_t r = static_cast<int64_t>(jb.x) * kRowsPerGroup + lr;
-  if (r >= R) return;
-  const int64_t orow = (r / grp) * hq + static_cast<int64_t>(g) * grp + static_cast<int>(r % grp);
-  f32x4* dst = reinterpret_cast<f32x4*>(dq + orow * D + 4 * sub);
-  f32x4 acc = overwrite ? f32x4{0.f, 0.f, 0.f, 0.f} : *dst;
-  for (int k = 0; k < jb.z; ++k)
-    acc += *reinterpret_cast<const f32x4*>(
-        sp.part_o + ((static_cast<int64_t>(jb.y + k) * hkv + g) * kRowsPerGroup + lr) * D + 4 * sub);
-  *dst = acc;
+  for (int sg = 0; sg < sp.max_pieces / 2; ++sg) {
+    const int4 jb = sp.groups[sg];
+    if (jb.x < 0) break;  // used entries come first
+    const int64_t r = static_cast<int64_t>(jb.x) * kRowsPerGroup + lr;
+    if (r >= R) continue;
+    const int64_t orow = (r / grp) * hq + static_cast<int64_t>(g) * grp + static_cast<int>(r % grp);
+    f32x4* dst = reinterpret_cast<f32x4*>(dq + orow * D + 4 * sub);
+    f32x4 acc = overwrite ? f32x4{0.f, 0.f, 0.f, 0.f} : *dst;
+    for (int k = 0; k < jb.z; ++k)
+      acc += *reinterpret_cast<const f32x4*>(
+          sp.part_o + ((static_cast<int64_t>(jb.y + k) * hkv + g) * kRowsPerGroup + lr) * D + 4 * sub);
+    *dst = acc;
+  }
 }
 
 // ============================================================================ dkdv kernel
@@ -1049,8 +1051,8 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
       dq_bf16_kernel<D><<<dim3(static_cast<unsigned>((groups + sp.max_pieces) * a.hkv)), dim3(64 * kDqWaves), 0, s>>>(p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       constexpr int kRuns = kRowsPerGroup / (256 / (D / 4));
-      dq_merge_kernel<D><<<dim3(static_cast<unsigned>(sp.max_pieces / 2 * a.hkv * kRuns)), dim3(256), 0, s>>>(
-          sp, a.dq, a.n_blk, a.hq, a.hkv, p.dq_overwrite);
+      dq_merge_kernel<D><<<dim3(static_cast<unsigned>(a.hkv * kRuns)), dim3(256), 0, s>>>(sp, a.dq, a.n_blk, a.hq,
+                                                                                          a.hkv, p.dq_overwrite);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       p.jobs = nullptr;
     } else if (a.workspace != nullptr && groups <= kMaxOrderedGroups) {

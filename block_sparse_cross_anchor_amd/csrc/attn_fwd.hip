@@ -407,13 +407,15 @@ fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-// Merge of a split row group's pieces.  One workgroup per (split group, kv head,
-// run of kMergeRowsPerLane * 256 / (d / 4) rows); d / 4 lanes share a row, each
-// lane takes kMergeRowsPerLane rows in one pass (rows merged in a loop would each
-// pay a round of memory latency; 4 rows per lane measured slower than 1).  Per
-// row: lse = M + ln sum_k exp(lse_k - M) with M the largest piece lse, and
-// O = sum_k exp(lse_k - lse) O_k; a row no piece reaches gets O = 0, lse = -inf.
-// Workgroups of unused split-group entries return at once.
+// Merge of the split row groups' pieces.  One workgroup per (kv head, run of
+// kMergeRowsPerLane * 256 / (d / 4) rows), looping over the split groups until the
+// first unused entry; d / 4 lanes share a row, each lane takes kMergeRowsPerLane rows
+// in one pass (rows merged in a loop would each pay a round of memory latency; 4 rows
+// per lane measured slower than 1).  Per row: lse = M + ln sum_k exp(lse_k - M) with
+// M the largest piece lse, and O = sum_k exp(lse_k - lse) O_k; a row no piece
+// reaches gets O = 0, lse = -inf.  The grid is small and fixed, so a call that split
+// nothing pays one short launch (a grid per possible split group was thousands of
+// workgroups, each waiting for a compute unit the other stream's kernel held).
 constexpr int kMergeRowsPerLane = 1;
 
 template <int D, bool OUT_BF16>
@@ -422,55 +424,56 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(RowSplit sp, void* o, fl
   constexpr int LPR = D / 4;                      // lanes per row, 4 values each
   constexpr int RPL = kMergeRowsPerLane;
   constexpr int RPW = 256 / LPR * RPL;            // rows per workgroup
-  constexpr int RUNS = kRowsPerGroup / RPW;       // workgroups per (split group, kv head)
   const int g = blockIdx.x % hkv;
-  const int run = (blockIdx.x / hkv) % RUNS;
-  const int4 jb = sp.groups[blockIdx.x / hkv / RUNS];
-  if (jb.x < 0) return;
+  const int run = blockIdx.x / hkv;  // < kRowsPerGroup / RPW
   const int grp = hq / hkv;
   const int64_t R = static_cast<int64_t>(n_blk) * kBlock * grp;
   const int sub = threadIdx.x % LPR;
   int lr[RPL];
 #pragma unroll
   for (int i = 0; i < RPL; ++i) lr[i] = run * RPW + i * (256 / LPR) + threadIdx.x / LPR;  // < kRowsPerGroup
-  auto prow = [&](int k, int i) { return (static_cast<int64_t>(jb.y + k) * hkv + g) * kRowsPerGroup + lr[i]; };
-  // one pass over the pieces with a running maximum, so each piece's lse and O are
-  // loaded together: den and acc are rescaled when the maximum grows
-  float mx[RPL], den[RPL];
-  f32x4 acc[RPL];
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    mx[i] = -INFINITY;
-    den[i] = 0.f;
-    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll 2
-  for (int k = 0; k < jb.z; ++k)
+  for (int sg = 0; sg < sp.max_pieces / 2; ++sg) {
+    const int4 jb = sp.groups[sg];
+    if (jb.x < 0) break;  // used entries come first
+    auto prow = [&](int k, int i) { return (static_cast<int64_t>(jb.y + k) * hkv + g) * kRowsPerGroup + lr[i]; };
+    // one pass over the pieces with a running maximum, so each piece's lse and O are
+    // loaded together: den and acc are rescaled when the maximum grows
+    float mx[RPL], den[RPL];
+    f32x4 acc[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const float lk = sp.part_lse[prow(k, i)];
-      const f32x4 ok = *reinterpret_cast<const f32x4*>(sp.part_o + prow(k, i) * D + 4 * sub);
-      if (lk == -INFINITY) continue;  // an empty piece adds nothing
-      const float mnew = fmaxf(mx[i], lk);
-      const float c = expf(mx[i] - mnew);  // 0 while mx is -inf
-      const float wk = expf(lk - mnew);
-      den[i] = den[i] * c + wk;
-      acc[i] = acc[i] * c + wk * ok;
-      mx[i] = mnew;
+      mx[i] = -INFINITY;
+      den[i] = 0.f;
+      acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll 2
+    for (int k = 0; k < jb.z; ++k)
 #pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    const int64_t r = static_cast<int64_t>(jb.x) * kRowsPerGroup + lr[i];
-    if (r >= R) continue;
-    const f32x4 out = acc[i] * (den[i] > 0.f ? 1.f / den[i] : 0.f);
-    const int64_t orow = (r / grp) * hq + static_cast<int64_t>(g) * grp + static_cast<int>(r % grp);
-    if (sub == 0) lse[orow] = den[i] > 0.f ? mx[i] + logf(den[i]) : -INFINITY;
-    if constexpr (OUT_BF16) {
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow * D + 4 * sub) = u32x2{
-          static_cast<uint32_t>(f32_to_bf16_bits(out[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(out[1])) << 16),
-          static_cast<uint32_t>(f32_to_bf16_bits(out[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(out[3])) << 16)};
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow * D + 4 * sub) = out;
+      for (int i = 0; i < RPL; ++i) {
+        const float lk = sp.part_lse[prow(k, i)];
+        const f32x4 ok = *reinterpret_cast<const f32x4*>(sp.part_o + prow(k, i) * D + 4 * sub);
+        if (lk == -INFINITY) continue;  // an empty piece adds nothing
+        const float mnew = fmaxf(mx[i], lk);
+        const float c = expf(mx[i] - mnew);  // 0 while mx is -inf
+        const float wk = expf(lk - mnew);
+        den[i] = den[i] * c + wk;
+        acc[i] = acc[i] * c + wk * ok;
+        mx[i] = mnew;
+      }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int64_t r = static_cast<int64_t>(jb.x) * kRowsPerGroup + lr[i];
+      if (r >= R) continue;
+      const f32x4 out = acc[i] * (den[i] > 0.f ? 1.f / den[i] : 0.f);
+      const int64_t orow = (r / grp) * hq + static_cast<int64_t>(g) * grp + static_cast<int>(r % grp);
+      if (sub == 0) lse[orow] = den[i] > 0.f ? mx[i] + logf(den[i]) : -INFINITY;
+      if constexpr (OUT_BF16) {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow * D + 4 * sub) = u32x2{
+            static_cast<uint32_t>(f32_to_bf16_bits(out[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(out[1])) << 16),
+            static_cast<uint32_t>(f32_to_bf16_bits(out[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(out[3])) << 16)};
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow * D + 4 * sub) = out;
+      }
     }
   }
 }
@@ -530,8 +533,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     constexpr int kRuns = kRowsPerGroup / (256 / (D / 4) * kMergeRowsPerLane);
     fwd_merge_kernel<D, OUT_BF16>
-        <<<dim3(static_cast<unsigned>(sp.max_pieces / 2 * a.hkv * kRuns)), dim3(256), 0, s>>>(sp, a.o, a.lse, a.n_blk,
-                                                                                           a.hq, a.hkv);
+        <<<dim3(static_cast<unsigned>(a.hkv * kRuns)), dim3(256), 0, s>>>(sp, a.o, a.lse, a.n_blk, a.hq, a.hkv);
     return hipGetLastError();
   }
   if (p.rg_order != nullptr) {
