@@ -1048,7 +1048,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
       if ((e = launch_row_split_plan(a, sp, s)) != hipSuccess) return e;
       p.jobs = sp.jobs;
       p.part_dq = sp.part_o;
-      dq_bf16_kernel<D><<<dim3(static_cast<unsigned>((groups + sp.max_pieces) * a.hkv)), dim3(64 * kDqWaves), 0, s>>>(p);
+      dq_bf16_kernel<D><<<dim3(static_cast<unsigned>((groups + sp.max_extra) * a.hkv)), dim3(64 * kDqWaves), 0, s>>>(p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       constexpr int kRuns = kRowsPerGroup / (256 / (D / 4));
       dq_merge_kernel<D><<<dim3(static_cast<unsigned>(a.hkv * kRuns)), dim3(256), 0, s>>>(sp, a.dq, a.n_blk, a.hq,

@@ -528,7 +528,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
     p.part_o = sp.part_o;
     p.part_lse = sp.part_lse;
     fwd_bf16_kernel<D, kNT, kWaves, kStages, OUT_BF16>
-        <<<dim3(static_cast<unsigned>((groups + sp.max_pieces) * a.hkv)), dim3(64 * kWaves), 0, s>>>(p);
+        <<<dim3(static_cast<unsigned>((groups + sp.max_extra) * a.hkv)), dim3(64 * kWaves), 0, s>>>(p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int kRuns = kRowsPerGroup / (256 / (D / 4) * kMergeRowsPerLane);

@@ -70,11 +70,16 @@ struct RowSplit {
   float* part_o;    // [max_pieces][hkv][kRowsPerGroup][d] forward: normalised partial O;
                     // dQ phase: the piece's scaled dQ sum
   int32_t max_pieces;
+  int32_t max_extra;  // jobs beyond one per row group, per kv head (the grid's spare slots)
 };
 constexpr int kMinSplitTiles = 16;
 // Pieces of split row groups per kv head: the cap is above the mean tiles per compute
 // unit, so they never exceed 2 n_cu / hkv.
 int32_t row_split_max_pieces(int32_t hkv, int32_t n_cu);
+// Jobs a split adds (a group of T > cap tiles becomes ceil(T / cap) < T / cap + 1
+// jobs, and the tiles of all groups sum to at most cap * 2 n_cu / (3 hkv)), so at most
+// ceil(2 n_cu / (3 hkv)) per kv head; the grid carries that many spare job slots.
+int32_t row_split_max_extra(int32_t hkv, int32_t n_cu);
 // Bytes of the split forward's scratch (0 if not representable or beyond the
 // ordered-group limit).
 int64_t row_split_bytes(int32_t n_blk, int32_t hq, int32_t hkv, int32_t d, int32_t n_cu);

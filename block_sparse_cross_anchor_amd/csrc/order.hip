@@ -132,11 +132,12 @@ __global__ __launch_bounds__(kOrderThreads) void row_split_plan_kernel(AttnArgs 
   __shared__ int cgs[kLdsChunks], clen[kLdsChunks];
   __shared__ int hist[kLenBuckets], tmp[kOrderThreads / 64];
   __shared__ unsigned long long total;
-  __shared__ int n_split_pieces, n_jobs;
+  __shared__ int n_split_pieces, n_cut_groups, n_jobs;
   const int tid = threadIdx.x;
   if (tid == 0) {
     total = 0;
     n_split_pieces = 0;
+    n_cut_groups = 0;
     n_jobs = 0;
   }
   for (int b = tid; b < kLenBuckets; b += kOrderThreads) hist[b] = 0;
@@ -152,10 +153,14 @@ __global__ __launch_bounds__(kOrderThreads) void row_split_plan_kernel(AttnArgs 
   for (int i = tid; i < n_groups; i += kOrderThreads) {
     const int n = cost[i] > cap ? (cost[i] + cap - 1) / cap : 1;
     pieces[i] = n;
-    if (n > 1) atomicAdd(&n_split_pieces, n);
+    if (n > 1) {
+      atomicAdd(&n_split_pieces, n);
+      atomicAdd(&n_cut_groups, 1);
+    }
   }
   __syncthreads();
-  const bool split_ok = n_split_pieces <= sp.max_pieces;  // holds by the choice of cap; kept as a guard
+  // both hold by the choice of cap; kept as guards (the grid has max_extra spare slots)
+  const bool split_ok = n_split_pieces <= sp.max_pieces && n_split_pieces - n_cut_groups <= sp.max_extra;
   auto bucket = [&](int L) {
     const int b = cap < kLenBuckets ? L : static_cast<int>(static_cast<int64_t>(L) * (kLenBuckets - 1) / cap);
     return kLenBuckets - 1 - min(b, kLenBuckets - 1);  // longest first
@@ -207,6 +212,7 @@ int n_compute_units() {
 }
 
 int32_t row_split_max_pieces(int32_t hkv, int32_t n_cu) { return max(2, (2 * n_cu + hkv - 1) / hkv); }
+int32_t row_split_max_extra(int32_t hkv, int32_t n_cu) { return max(1, (2 * n_cu + 3 * hkv - 1) / (3 * hkv)); }
 
 namespace {
 struct SplitLayout {
@@ -244,6 +250,7 @@ RowSplit row_split_layout(void* ws, const AttnArgs& a) {
   sp.part_lse = reinterpret_cast<float*>(b + L.lse_off);
   sp.part_o = reinterpret_cast<float*>(b + L.o_off);
   sp.max_pieces = pieces;
+  sp.max_extra = row_split_max_extra(a.hkv, a.n_cu);
   return sp;
 }
 

@@ -54,7 +54,15 @@ def read_plan(n_groups, hkv):
     ws = sxattn._workspaces[("fwd_split", torch.device("cuda", torch.cuda.current_device()),
                              torch.cuda.current_stream().cuda_stream)]
     jobs = ws[:16 * (n_groups + pieces)].cpu().numpy().view(np.int32).reshape(-1, 4)
+    assert (jobs[:, 0] >= 0).sum() <= n_groups + max_extra(hkv)
     return jobs, pieces
+
+
+def max_extra(hkv):
+    """Spare job slots of the split grid per kv head: a group of T > cap tiles becomes
+    ceil(T / cap) jobs and the tiles of all groups sum to at most cap 2 n_cu / (3 hkv)."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    return max(1, -(-2 * n_cu // (3 * hkv)))
 
 
 def check_plan(jobs, pieces, tiles):
@@ -227,6 +235,7 @@ def test_split_dq_matches_unsplit_and_oracle(case):
     ws = sxattn._workspaces[("bwd_split", torch.device("cuda", torch.cuda.current_device()),
                              torch.cuda.current_stream().cuda_stream)]
     jobs = ws[base:base + 16 * (len(tiles) + pieces)].cpu().numpy().view(np.int32).reshape(-1, 4)
+    assert (jobs[:, 0] >= 0).sum() <= len(tiles) + max_extra(hkv)
     assert check_plan(jobs, pieces, tiles) > 0
     dq_u = host64(out["auto", "over"])
     assert np.abs(dq_u).max() > 0
