@@ -8,10 +8,9 @@ tokens and planned onto 8 virtual devices ("bins"):
   1. chunk_cost   realised cost of each chunk (GPU, int64)
   2. lpt_plan     longest-processing-time-first plan with equal chunk counts (GPU; the
                   same plan as the host lpt_assign, so nothing returns to the host)
-  3. context_gather of every bin's chunks of K and V into the bins' local buffers
-     (one call per tensor), then per bin sparse_xattn_fwd (the own-block term on bin
-     0): partial O, lse; the bins alternate between two streams, so one bin's forward
-     overlaps the other stream's ordering pass and the tail of its forward
+  3. per bin: context_gather of its chunks of K and V into its local buffer, then
+     sparse_xattn_fwd (the own-block term on bin 0): partial O, lse; the bins
+     alternate between two streams, so their gathers and forwards overlap
   4. lse_combine  of the 8 partials
   5. sparse_xattn_bwd: delta pre-pass, then the dQ phase of every bin (accumulated,
      on a second stream) beside the dK/dV phase of every bin (bf16 dK, dV)
@@ -171,9 +170,9 @@ def build_problem(torch, seed, split=False, inputs=None, bwd_schedule="overlap")
     P["plan_gs"], P["plan_gl"] = P["plan"][0], P["plan"][1]
     P["per_bin"], P["n_loc"] = per_bin, n_loc
     P["scale"] = 1.0 / math.sqrt(d)
-    # The bins' forwards alternate between the current stream and a second one
-    # (default priority), so one bin's forward overlaps the other stream's ordering
-    # pass and the tail of its forward.  Each stream has its own forward
+    # The bins' gathers and forwards alternate between the current stream and a
+    # second one (default priority), so one bin's forward overlaps the other
+    # stream's gather and the tail of its forward.  Each stream has its own forward
     # workspace; the two events that fork and join the streams are created here,
     # outside any timed region.
     P["side_stream"] = torch.cuda.Stream()
@@ -305,18 +304,15 @@ def post_plan(torch, P, T, bins_np, cost_np, order):
     fwd_pairs = int(cost_np.sum()) + self_pairs
 
     def gathers_and_forwards():
-        # Every bin's context in one gather per tensor: the plan lists the bins' chunks
-        # back to back in bin order, and the local buffers hold the bins back to back.
-        # The side stream starts after the gathers (and after everything the previous
-        # step queued on the current stream, which reads the buffers they rewrite); the
-        # current stream continues once both are done.
-        for src, dst in ((P["k"], P["k_loc"]), (P["v"], P["v_loc"])):
-            sxattn.context_gather(src, P["plan_gs"].reshape(-1), P["plan_gl"].reshape(-1), nb * n_loc,
-                                  out=dst.view((nb * n_loc,) + tuple(dst.shape[2:])))
+        # the side stream starts after the plan upload (and after everything the
+        # previous step queued on the current stream, which reads the buffers it
+        # rewrites); the current stream continues once both are done
         P["ev_fork"].record(main)
         side.wait_event(P["ev_fork"])
         for b in range(nb):
             with torch.cuda.stream(main if b % 2 == 0 else side):
+                for src, dst in ((P["k"], P["k_loc"][b]), (P["v"], P["v_loc"][b])):
+                    sxattn.context_gather(src, P["plan_gs"][b], P["plan_gl"][b], n_loc, out=dst)
                 sxattn.sparse_xattn_fwd(
                     P["q"], P["k_loc"][b], P["v_loc"][b], metas[b], scale,
                     P["ks"] if b == 0 else None, P["vs"] if b == 0 else None,
@@ -997,8 +993,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "kernels_note": f"per-phase times from {n_bd} warm-up steps with events around every phase; "
-                        "gather_fwd is the context gathers (one per tensor for all bins) and the bins' "
-                        "forwards on two streams, its rate the forward's FLOP over that span; " + {
+                        "gather_fwd is the bins' context gathers and forwards on two streams, its "
+                        "rate the forward's FLOP over that span; " + {
                             "halves": "bwd_dq runs two halves of the query blocks on two streams",
                             "serial": "bwd_dq then bwd_dkdv on one stream",
                             "overlap": "bwd_dq runs on a second stream beside bwd_dkdv, so their "
