@@ -360,7 +360,9 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(RowSplit sp, float* dq, i
 // Schedule.  The work is the list of (kv head, tile, hit step) triples, and a key
 // tile near the start of a long sample is hit by many times more steps than the
 // average one.  With a workspace, a count pass gives every tile its number of hit
-// steps and the kernel runs one workgroup per compute unit, each taking an equal
+// steps and their list in order (a segment's steps are then read from the list, not
+// found by scanning every step of the kv head), and the kernel runs one workgroup
+// per compute unit, each taking an equal
 // contiguous share of the list ("stream-K"): inside a share only the first and the
 // last tile can be partial; their fp32 sums go to the share's two workspace slots and
 // a reduce pass adds the slots of each such tile.  Tiles a share covers whole are
@@ -379,6 +381,7 @@ constexpr int kStageBufs = 2 * kStepsPerSync;          // LDS stages: one group 
 constexpr int kKeysPerWG = kKeysPerWave * kKvWaves;
 constexpr int kStepRows = 32;
 constexpr int kListCap = 2 * 64 * kKvWaves;  // step indices held in LDS at once
+static_assert(kListCap % (64 * kKvWaves) == 0, "a list batch splits evenly over the threads");
 
 // Stream-K list units: a tile with hits occupies kSetupUnits + hits consecutive units
 // of the per-head list (the first ones stand for its setup, step list and write-back,
@@ -393,6 +396,8 @@ struct DkdvSched {
   const int32_t* prefix;   // [n_tiles + 1]: first list unit of each tile (per kv head)
   const int4* tinfo;       // [n_tiles]: key-coordinate range (x, y), hit steps (z) and first hit step (w)
   const int32_t* coord;    // [n_loc]: global key coordinate of each local context row
+  int32_t* hits;           // [n_tiles][hit_stride]: the hit steps of each tile, in order
+  int64_t hit_stride;      // query steps of a kv head (the most hits a tile can have)
   float* slots;            // [2 n_shares][kKeysPerWG][2][D]: partial dK, dV
 };
 
@@ -475,19 +480,31 @@ __global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched 
   __syncthreads();
   kmin = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
   kmax = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+  // hit steps in increasing order: batch by batch, each hit at (hits before the batch)
+  // + (hits of lower waves) + (hits of lower lanes)
+  int32_t* list = sc.hits + static_cast<int64_t>(t) * sc.hit_stride;
   int n = 0, first = sg.n_steps;
   for (int base = 0; base < sg.n_steps; base += 256) {
     const bool hit = step_hit(p, sg, base + tid, n_q, self_tile, kmin, kmax);
-    const int cnt = __syncthreads_count(hit);
-    if (cnt > 0 && first == sg.n_steps) {  // first hit of this batch: smallest hitting thread
-      const uint64_t m = __ballot(hit);
-      if (tid % 64 == 0) red[0][wave] = m ? base + 64 * wave + __builtin_ctzll(m) : 0x7fffffff;
-      __syncthreads();
-      first = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
-      __syncthreads();
+    const uint64_t m = __ballot(hit);
+    __syncthreads();  // the previous batch's reads of red are done
+    if (tid % 64 == 0) red[0][wave] = __popcll(m);
+    __syncthreads();
+    int pre = 0, cnt = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      pre += w2 < wave ? red[0][w2] : 0;
+      cnt += red[0][w2];
+    }
+    if (hit) {
+      const int pos = n + pre + __popcll(m & ((uint64_t{1} << (tid % 64)) - 1));
+      list[pos] = base + tid;
+      if (pos == 0) red[1][0] = base + tid;  // the first hit (read after the loop)
     }
     n += cnt;
   }
+  __syncthreads();
+  if (n > 0) first = red[1][0];
   if (tid == 0) {
     prefix[t + 1] = n > 0 ? n + kSetupUnits : 0;
     tinfo[t] = int4{kmin, kmax, n, first};
@@ -677,6 +694,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
           kf[hh][ks] = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(K + (krc[hh] * p.hkv + g) * D + 16 * ks + 8 * h2));
     }
+    // Stream-K: the segment's first batch of hit steps [s0, s0 + cnt0) from the count
+    // pass's list, loaded beside the tile loads (before the accumulators are live);
+    // later batches, if any, are collected by the scan below.
+    int cnt0 = 0;
+    if (streamk) {
+      cnt0 = min(kListCap, s1 - s0);
+      const int32_t* list = sc.hits + static_cast<int64_t>(t) * sc.hit_stride + s0;
+#pragma unroll
+      for (int k = 0; k < kListCap / kT; ++k) {
+        const int i = k * kT + tid;
+        if (i < cnt0) {
+          const int st = list[i];
+          const int tk = sg.tok0(st);
+          const int b0 = tk / kBlock, b1 = (tk + sg.ntok(st, n_q) - 1) / kBlock;
+          step_list[i] = st;
+          step_iv[i] = self_tile ? int4{kBlock * b0, kBlock * b0 + kBlock, kBlock * b1, kBlock * b1 + kBlock}
+                                 : int4{p.sample_start[b0], p.anchor[b0], p.sample_start[b1], p.anchor[b1]};
+        }
+      }
+    }
     wait_vmcnt<0>();  // the segment's own loads are complete before the copy pipeline starts
     f32x16 dkacc[H][DT], dvacc[H][DT];
 #pragma unroll
@@ -708,10 +745,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
 
     int scan = scan0;  // next step to examine
     int ord = 0;       // hits of this tile before `scan`
+    bool listed = cnt0 > 0;  // the first batch is in LDS already
     while (scan < sg.n_steps && ord < s1) {
       // ---- collect the step indices of hits ord in [s0, s1), up to the list capacity
       int cnt = 0;
-      while (scan < sg.n_steps && ord < s1 && cnt <= kListCap - kT) {
+      const bool from_list = listed;
+      if (listed) {
+        lds_barrier();  // the listed batch is visible to every wave
+        cnt = cnt0;
+        ord = s0 + cnt0;                                                     // hits before `scan`
+        scan = __builtin_amdgcn_readfirstlane(step_list[cnt0 - 1]) + 1;  // past the last listed hit
+        listed = false;
+      }
+      while (!from_list && scan < sg.n_steps && ord < s1 && cnt <= kListCap - kT) {
         const int st = scan + tid;
         const bool hit = step_hit(p, sg, st, n_q, self_tile, kmin, kmax);
         const uint64_t m = __ballot(hit);
@@ -985,7 +1031,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, DkdvSched
 }
 
 struct WsLayout {
-  int64_t n_tiles, n_shares, prefix_off, tinfo_off, coord_off, order_off, slots_off, bytes;
+  int64_t n_tiles, n_shares, hit_stride, prefix_off, tinfo_off, coord_off, hits_off, order_off, slots_off, bytes;
 };
 
 WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d, int64_t grp) {
@@ -994,10 +1040,16 @@ WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d, int64_t grp) {
   L.n_tiles = (n_loc + kKeysPerWG - 1) / kKeysPerWG + (n_blk * kBlock + kKeysPerWG - 1) / kKeysPerWG;
   L.n_shares = n_compute_units();
   const int64_t groups = (n_blk * kBlock * grp + kRowsPerGroup - 1) / kRowsPerGroup;
+  {  // query steps of one kv head, as StepGeo counts them
+    const int64_t gs = grp < kStepRows ? grp : kStepRows, ts = kStepRows / gs;
+    const int64_t hcs = (grp + kStepRows - 1) / kStepRows;
+    L.hit_stride = (n_blk * kBlock + ts - 1) / ts * hcs;
+  }
   L.prefix_off = 0;
   L.tinfo_off = up(4 * (L.n_tiles + 1));
   L.coord_off = L.tinfo_off + up(16 * L.n_tiles);
-  L.order_off = L.coord_off + up(4 * n_loc);
+  L.hits_off = L.coord_off + up(4 * n_loc);
+  L.order_off = L.hits_off + up(4 * L.n_tiles * L.hit_stride);
   L.slots_off = L.order_off + up(4 * (groups < kMaxOrderedGroups ? groups : int64_t{kMaxOrderedGroups}));
   L.bytes = L.slots_off + 2 * L.n_shares * static_cast<int64_t>(kKeysPerWG) * 2 * d * 4;
   return L;
@@ -1079,6 +1131,8 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   sc.prefix = nullptr;
   sc.tinfo = nullptr;
   sc.coord = nullptr;
+  sc.hits = nullptr;
+  sc.hit_stride = 0;
   sc.slots = nullptr;
   if (a.workspace != nullptr) {
     const WsLayout L = ws_layout(a.n_blk, a.n_loc, D, a.hq / a.hkv);
@@ -1090,6 +1144,8 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
     sc.prefix = prefix;
     sc.tinfo = tinfo;
     sc.coord = coord;
+    sc.hits = reinterpret_cast<int32_t*>(ws + L.hits_off);
+    sc.hit_stride = L.hit_stride;
     sc.slots = reinterpret_cast<float*>(ws + L.slots_off);
     dkdv_count_kernel<<<dim3(static_cast<unsigned>(n_tiles)), dim3(256), 0, s>>>(p, sc, prefix, tinfo, coord);
     if ((e = hipGetLastError()) != hipSuccess) return e;
