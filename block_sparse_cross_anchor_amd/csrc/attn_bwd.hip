@@ -396,6 +396,7 @@ struct DkdvSched {
   const int32_t* prefix;   // [n_tiles + 1]: first list unit of each tile (per kv head)
   const int4* tinfo;       // [n_tiles]: key-coordinate range (x, y), hit steps (z) and first hit step (w)
   const int32_t* coord;    // [n_loc]: global key coordinate of each local context row
+  const int32_t* share_tile;  // [n_shares]: tile holding each share's first list unit
   int32_t* hits;           // [n_tiles][hit_stride]: the hit steps of each tile, in order
   int64_t hit_stride;      // query steps of a kv head (the most hits a tile can have)
   float* slots;            // [2 n_shares][kKeysPerWG][2][D]: partial dK, dV
@@ -512,8 +513,12 @@ __global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched 
   }
 }
 
-// In-place inclusive scan of prefix[1 .. n] (one workgroup of 1024 threads).
-__global__ __launch_bounds__(1024) void dkdv_scan_kernel(int32_t* prefix, int n) {
+// In-place inclusive scan of prefix[1 .. n] (one workgroup of 1024 threads), then the
+// tile holding each stream-K share's first list unit (the largest tile t with
+// prefix[t] <= the unit's offset in its kv head's list), so that a share starts
+// without a search of its own.
+__global__ __launch_bounds__(1024) void dkdv_scan_kernel(int32_t* prefix, int n, int32_t* share_tile, int n_shares,
+                                                         int hkv) {
   __shared__ int part[1024];
   const int tid = threadIdx.x;
   const int per = (n + 1023) / 1024;
@@ -532,6 +537,18 @@ __global__ __launch_bounds__(1024) void dkdv_scan_kernel(int32_t* prefix, int n)
   for (int i = a; i < e; ++i) {
     run += prefix[i];
     prefix[i] = run;
+  }
+  __syncthreads();  // the scanned prefix is visible to the whole workgroup
+  const int64_t W = prefix[n], tot = W * hkv;
+  for (int j = tid; j < n_shares && W > 0; j += 1024) {
+    const int r = static_cast<int>((static_cast<int64_t>(j) * tot / n_shares) % W);
+    int lo = 0, hi = n;  // prefix[lo] <= r < prefix[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (prefix[mid] <= r) lo = mid;
+      else hi = mid;
+    }
+    share_tile[j] = lo;
   }
 }
 
@@ -579,19 +596,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
   };
 
   bool first_seg = true;  // no segment with steps yet in this share
-  // (head, tile) holding list unit `pos`: a binary search for the share's first unit;
-  // later segments are the following tiles, so the walk below only steps forward
+  // (head, tile) holding list unit `pos`, the tile from the scan pass; later segments
+  // are the following tiles, so the walk below only steps forward
   int g = 0, t = 0;
   if (streamk && pos < end) {
     g = static_cast<int>(pos / W);
-    const int r = static_cast<int>(pos % W);
-    int lo = 0, hi = sc.n_tiles;  // prefix[lo] <= r < prefix[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (ld_uniform(sc.prefix, mid) <= r) lo = mid;
-      else hi = mid;
-    }
-    t = lo;
+    t = ld_uniform(sc.share_tile, share);
   }
   while (pos < end) {
     int s0, s1, hits = 0;
@@ -1031,7 +1041,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, DkdvSched
 }
 
 struct WsLayout {
-  int64_t n_tiles, n_shares, hit_stride, prefix_off, tinfo_off, coord_off, hits_off, order_off, slots_off, bytes;
+  int64_t n_tiles, n_shares, hit_stride, prefix_off, tinfo_off, coord_off, share_off, hits_off, order_off, slots_off,
+      bytes;
 };
 
 WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d, int64_t grp) {
@@ -1048,7 +1059,8 @@ WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d, int64_t grp) {
   L.prefix_off = 0;
   L.tinfo_off = up(4 * (L.n_tiles + 1));
   L.coord_off = L.tinfo_off + up(16 * L.n_tiles);
-  L.hits_off = L.coord_off + up(4 * n_loc);
+  L.share_off = L.coord_off + up(4 * n_loc);
+  L.hits_off = L.share_off + up(4 * L.n_shares);
   L.order_off = L.hits_off + up(4 * L.n_tiles * L.hit_stride);
   L.slots_off = L.order_off + up(4 * (groups < kMaxOrderedGroups ? groups : int64_t{kMaxOrderedGroups}));
   L.bytes = L.slots_off + 2 * L.n_shares * static_cast<int64_t>(kKeysPerWG) * 2 * d * 4;
@@ -1131,6 +1143,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   sc.prefix = nullptr;
   sc.tinfo = nullptr;
   sc.coord = nullptr;
+  sc.share_tile = nullptr;
   sc.hits = nullptr;
   sc.hit_stride = 0;
   sc.slots = nullptr;
@@ -1144,12 +1157,15 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
     sc.prefix = prefix;
     sc.tinfo = tinfo;
     sc.coord = coord;
+    int32_t* share_tile = reinterpret_cast<int32_t*>(ws + L.share_off);
+    sc.share_tile = share_tile;
     sc.hits = reinterpret_cast<int32_t*>(ws + L.hits_off);
     sc.hit_stride = L.hit_stride;
     sc.slots = reinterpret_cast<float*>(ws + L.slots_off);
     dkdv_count_kernel<<<dim3(static_cast<unsigned>(n_tiles)), dim3(256), 0, s>>>(p, sc, prefix, tinfo, coord);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dkdv_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(prefix, static_cast<int>(n_tiles));
+    dkdv_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(prefix, static_cast<int>(n_tiles), share_tile,
+                                                    static_cast<int>(L.n_shares), a.hkv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     dkdv_bf16_kernel<D><<<dim3(static_cast<unsigned>(L.n_shares)), dim3(64 * kKvWaves), 0, s>>>(p, sc);
     if ((e = hipGetLastError()) != hipSuccess) return e;
