@@ -336,3 +336,57 @@ def test_bwd_bf16_key_value_gradients(workspace):
                                            dv=torch.full(k.shape, 3.0, device="cuda").to(torch.bfloat16))
     torch.cuda.synchronize()
     assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+
+def longest_stream_k_segment(meta, n_blk, grp, n_ctx, n_shares, setup=10):
+    """Hits of the longest segment the load-balanced dK/dV phase gives one share, for a
+    single sample starting at token 0 and one kv head: per 256-key tile the query
+    steps (32 rows from a token boundary) whose blocks read past the tile's first
+    key, each hit tile also carrying `setup` list units, the list cut into n_shares
+    equal parts."""
+    ts = 32 // min(grp, 32)
+    hcs = -(-grp // 32)
+    n_q = 16 * n_blk
+    t0 = np.arange(-(-n_q // ts)) * ts
+    last = np.minimum(t0 + ts, n_q) - 1
+    reach = np.repeat(np.maximum(meta.anchor[t0 // 16], meta.anchor[last // 16]).astype(np.int64), hcs)
+    hits = (reach[None, :] > 256 * np.arange(n_ctx // 256)[:, None]).sum(1)
+    units = (hits + setup) * (hits > 0)
+    pre = np.concatenate([[0], np.cumsum(units)])
+    j = np.arange(n_shares)
+    a, e = j * pre[-1] // n_shares, (j + 1) * pre[-1] // n_shares
+    seg = np.minimum(e[:, None], pre[1:][None]) - np.maximum(a[:, None], pre[:-1][None] + setup)
+    return int(np.where(hits[None] > 0, seg, 0).max())
+
+
+@pytest.mark.parametrize("hq,n_blk", [(40, 160), (8, 1536)])
+def test_dkdv_stream_k_segments_longer_than_one_step_batch(hq, n_blk):
+    """Stream-K segments of more than 1024 hit steps: a segment loads its first 1024
+    steps from the count pass's list and collects the rest by scanning from the last
+    listed step.  One 32768-token sample read by every block, one kv head (so the
+    shares are long), a head group beyond the 32-row step (40) and within it (8): the
+    load-balanced dK/dV phase must give the sums of the one-workgroup-per-tile phase
+    (which only scans), to float32 summation order."""
+    hkv, d, n_ctx = 1, 64, 32768
+    meta = synth.draw_meta(31 + hq, n_ctx, n_ctx, n_ctx, n_blk)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert longest_stream_k_segment(meta, n_blk, hq // hkv, n_ctx, n_cu) > 1024
+    gs, gl = synth.contiguous_chunks(n_ctx, 1024)
+    inp = synth.draw_inputs(31 + hq, meta, hq, hkv, d, "bf16", 1.0 / math.sqrt(d), gs, gl, with_dout=True)
+    scale = 1.0 / math.sqrt(d)
+    dm = device_meta(meta, gs, gl)
+    o, lse = sxattn.sparse_xattn_fwd(dev(inp.q), dev(inp.k), dev(inp.v), dm, scale,
+                                     dev(inp.k_self), dev(inp.v_self))
+    out = {}
+    for ws in ("auto", None):
+        dq = torch.zeros(inp.q.shape, dtype=torch.float32, device="cuda")
+        dk, dv, dks, dvs = sxattn.sparse_xattn_bwd(dev(inp.q), dev(inp.k), dev(inp.v), dm, scale, o,
+                                                   dev(inp.dout), lse, dq, dev(inp.k_self),
+                                                   dev(inp.v_self), workspace=ws)
+        out[ws] = [host64(t) for t in (dk, dv, dks, dvs)]
+    torch.cuda.synchronize()
+    for got, want, name in zip(out["auto"], out[None], ("dk", "dv", "dk_self", "dv_self")):
+        assert np.abs(want).max() > 0
+        err = rel_frob(got, want)
+        assert err <= 1e-5, f"{name}: relative Frobenius difference {err:.3e}"
