@@ -591,7 +591,7 @@ def balance_study(torch, workload, seed, reps):
     bf, f32 = torch.bfloat16, torch.float32
     k_loc = torch.empty((n_loc, hkv, d), dtype=bf, device="cuda")
     v_loc = torch.empty_like(k_loc)
-    dk = torch.empty((n_loc, hkv, d), dtype=f32, device="cuda")
+    dk = torch.empty((n_loc, hkv, d), dtype=bf, device="cuda")   # bf16 gradients, as in the step
     dv = torch.empty_like(dk)
     o_p = torch.empty((n_q, hq, d), dtype=bf, device="cuda")
     lse_p = torch.empty((n_q, hq), dtype=f32, device="cuda")
@@ -667,8 +667,12 @@ def balance_study(torch, workload, seed, reps):
             jobs = np.repeat(group_tiles[:, bins_np == b].sum(1), hkv)
             rows.append((name, b, {ph: ms[ph][b] for ph in phases}, tot[b],
                          {pn: loads[pn][b] for pn in preds}, jobs))
+        # the same totals with the forward and dQ phases on the split schedule
+        tot_split = [ms["fwd_split"][b] + ms["dq_split"][b] + ms["dkdv"][b] for b in range(nb)]
         out["plans"][name] = {
             "max_bin_ms": round(max(tot), 4), "mean_bin_ms": round(float(np.mean(tot)), 4),
+            "max_bin_ms_split": round(max(tot_split), 4),
+            "mean_bin_ms_split": round(float(np.mean(tot_split)), 4),
             "time_imbalance": round(max(tot) / float(np.mean(tot)) - 1, 4),
             "phase_max_ms": {ph: round(max(ms[ph]), 4) for ph in phases},
             "load_imbalance": {pn: round(max(loads[pn]) / float(np.mean(loads[pn])) - 1, 4)
