@@ -398,6 +398,7 @@ struct DkdvSched {
   const int32_t* coord;    // [n_loc]: global key coordinate of each local context row
   const int32_t* share_tile;  // [n_shares]: tile holding each share's first list unit
   int32_t* hits;           // [n_tiles][hit_stride]: the hit steps of each tile, in order
+                           // (nullptr when the lists would exceed kMaxListEntries: then scanned)
   int64_t hit_stride;      // query steps of a kv head (the most hits a tile can have)
   float* slots;            // [2 n_shares][kKeysPerWG][2][D]: partial dK, dV
 };
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched 
   kmax = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
   // hit steps in increasing order: batch by batch, each hit at (hits before the batch)
   // + (hits of lower waves) + (hits of lower lanes)
-  int32_t* list = sc.hits + static_cast<int64_t>(t) * sc.hit_stride;
+  int32_t* list = sc.hits != nullptr ? sc.hits + static_cast<int64_t>(t) * sc.hit_stride : nullptr;
   int n = 0, first = sg.n_steps;
   for (int base = 0; base < sg.n_steps; base += 256) {
     const bool hit = step_hit(p, sg, base + tid, n_q, self_tile, kmin, kmax);
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched 
     }
     if (hit) {
       const int pos = n + pre + __popcll(m & ((uint64_t{1} << (tid % 64)) - 1));
-      list[pos] = base + tid;
+      if (list != nullptr) list[pos] = base + tid;
       if (pos == 0) red[1][0] = base + tid;  // the first hit (read after the loop)
     }
     n += cnt;
@@ -708,7 +709,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
     // pass's list, loaded beside the tile loads (before the accumulators are live);
     // later batches, if any, are collected by the scan below.
     int cnt0 = 0;
-    if (streamk) {
+    if (streamk && sc.hits != nullptr) {
       cnt0 = min(kListCap, s1 - s0);
       const int32_t* list = sc.hits + static_cast<int64_t>(t) * sc.hit_stride + s0;
 #pragma unroll
@@ -1040,9 +1041,13 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, DkdvSched
   }
 }
 
+// Hit lists are kept up to this many (tile, step) entries (256 MiB); larger calls scan.
+constexpr int64_t kMaxListEntries = int64_t{1} << 26;
+
 struct WsLayout {
   int64_t n_tiles, n_shares, hit_stride, prefix_off, tinfo_off, coord_off, share_off, hits_off, order_off, slots_off,
       bytes;
+  bool lists;
 };
 
 WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d, int64_t grp) {
@@ -1061,7 +1066,8 @@ WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d, int64_t grp) {
   L.coord_off = L.tinfo_off + up(16 * L.n_tiles);
   L.share_off = L.coord_off + up(4 * n_loc);
   L.hits_off = L.share_off + up(4 * L.n_shares);
-  L.order_off = L.hits_off + up(4 * L.n_tiles * L.hit_stride);
+  L.lists = L.n_tiles * L.hit_stride <= kMaxListEntries;
+  L.order_off = L.hits_off + (L.lists ? up(4 * L.n_tiles * L.hit_stride) : 0);
   L.slots_off = L.order_off + up(4 * (groups < kMaxOrderedGroups ? groups : int64_t{kMaxOrderedGroups}));
   L.bytes = L.slots_off + 2 * L.n_shares * static_cast<int64_t>(kKeysPerWG) * 2 * d * 4;
   return L;
@@ -1159,7 +1165,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
     sc.coord = coord;
     int32_t* share_tile = reinterpret_cast<int32_t*>(ws + L.share_off);
     sc.share_tile = share_tile;
-    sc.hits = reinterpret_cast<int32_t*>(ws + L.hits_off);
+    sc.hits = L.lists ? reinterpret_cast<int32_t*>(ws + L.hits_off) : nullptr;
     sc.hit_stride = L.hit_stride;
     sc.slots = reinterpret_cast<float*>(ws + L.slots_off);
     dkdv_count_kernel<<<dim3(static_cast<unsigned>(n_tiles)), dim3(256), 0, s>>>(p, sc, prefix, tinfo, coord);

@@ -390,3 +390,33 @@ def test_dkdv_stream_k_segments_longer_than_one_step_batch(hq, n_blk):
         assert np.abs(want).max() > 0
         err = rel_frob(got, want)
         assert err <= 1e-5, f"{name}: relative Frobenius difference {err:.3e}"
+
+
+def test_dkdv_stream_k_without_hit_lists():
+    """Calls whose (tile, query step) lists would exceed 2^26 entries keep no lists:
+    every stream-K segment then collects its steps by scanning.  A 1M-token context of
+    2048-token samples, 8192 queries, head group 40 (16384 query steps): the
+    load-balanced dK/dV phase must give the one-workgroup-per-tile phase's sums."""
+    hq, hkv, d, n_ctx, n_blk = 40, 1, 64, 1 << 20, 512
+    n_tiles = n_ctx // 256 + 16 * n_blk // 256
+    n_steps = 16 * n_blk * 2              # one token per step, two steps per token
+    assert n_tiles * n_steps > 1 << 26
+    meta = synth.draw_meta(77, n_ctx, 2048, 2048, n_blk)
+    gs, gl = synth.contiguous_chunks(n_ctx, 1024)
+    inp = synth.draw_inputs(77, meta, hq, hkv, d, "bf16", 1.0 / math.sqrt(d), gs, gl, with_dout=True)
+    scale = 1.0 / math.sqrt(d)
+    dm = device_meta(meta, gs, gl)
+    o, lse = sxattn.sparse_xattn_fwd(dev(inp.q), dev(inp.k), dev(inp.v), dm, scale,
+                                     dev(inp.k_self), dev(inp.v_self))
+    out = {}
+    for ws in ("auto", None):
+        dq = torch.zeros(inp.q.shape, dtype=torch.float32, device="cuda")
+        dk, dv, dks, dvs = sxattn.sparse_xattn_bwd(dev(inp.q), dev(inp.k), dev(inp.v), dm, scale, o,
+                                                   dev(inp.dout), lse, dq, dev(inp.k_self),
+                                                   dev(inp.v_self), workspace=ws)
+        out[ws] = [host64(t) for t in (dk, dv, dks, dvs)]
+    torch.cuda.synchronize()
+    for got, want, name in zip(out["auto"], out[None], ("dk", "dv", "dk_self", "dv_self")):
+        assert np.abs(want).max() > 0
+        err = rel_frob(got, want)
+        assert err <= 1e-5, f"{name}: relative Frobenius difference {err:.3e}"
