@@ -304,15 +304,19 @@ def post_plan(torch, P, T, bins_np, cost_np, order):
     fwd_pairs = int(cost_np.sum()) + self_pairs
 
     def gathers_and_forwards():
-        # the side stream starts after the plan upload (and after everything the
-        # previous step queued on the current stream, which reads the buffers it
-        # rewrites); the current stream continues once both are done
-        P["ev_fork"].record(main)
-        side.wait_event(P["ev_fork"])
+        # The side stream starts once bin 0's context is gathered (after the plan and
+        # after everything the previous step queued on the current stream, which reads
+        # the buffers the gathers rewrite), so the two streams run half a gather apart
+        # and one stream's gathers overlap the other's forward; the current stream
+        # continues once both are done.
         for b in range(nb):
             with torch.cuda.stream(main if b % 2 == 0 else side):
+                if b == 1:
+                    side.wait_event(P["ev_fork"])
                 for src, dst in ((P["k"], P["k_loc"][b]), (P["v"], P["v_loc"][b])):
                     sxattn.context_gather(src, P["plan_gs"][b], P["plan_gl"][b], n_loc, out=dst)
+                if b == 0:
+                    P["ev_fork"].record(main)
                 sxattn.sparse_xattn_fwd(
                     P["q"], P["k_loc"][b], P["v_loc"][b], metas[b], scale,
                     P["ks"] if b == 0 else None, P["vs"] if b == 0 else None,
