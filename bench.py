@@ -306,21 +306,28 @@ def post_plan(torch, P, T, bins_np, cost_np, order):
     def gathers_and_forwards():
         # The side stream starts once bin 0's context is gathered (after the plan and
         # after everything the previous step queued on the current stream, which reads
-        # the buffers the gathers rewrite), so the two streams run half a gather apart
-        # and one stream's gathers overlap the other's forward; the current stream
-        # continues once both are done.
+        # the buffers the gathers rewrite), so the two streams run half a gather apart.
+        # Each stream gathers its later bins right after its first forward, beside the
+        # other stream's forward; the current stream continues once both are done.
+        def gather(b):
+            for src, dst in ((P["k"], P["k_loc"][b]), (P["v"], P["v_loc"][b])):
+                sxattn.context_gather(src, P["plan_gs"][b], P["plan_gl"][b], n_loc, out=dst)
+
         for b in range(nb):
             with torch.cuda.stream(main if b % 2 == 0 else side):
                 if b == 1:
                     side.wait_event(P["ev_fork"])
-                for src, dst in ((P["k"], P["k_loc"][b]), (P["v"], P["v_loc"][b])):
-                    sxattn.context_gather(src, P["plan_gs"][b], P["plan_gl"][b], n_loc, out=dst)
+                if b < 2:
+                    gather(b)
                 if b == 0:
                     P["ev_fork"].record(main)
                 sxattn.sparse_xattn_fwd(
                     P["q"], P["k_loc"][b], P["v_loc"][b], metas[b], scale,
                     P["ks"] if b == 0 else None, P["vs"] if b == 0 else None,
                     out=P["o_parts"][b], lse=P["lse_parts"][b], workspace=P["fwd_ws"][b % 2])
+                if b < 2:  # the stream's later bins, beside the other stream's first forward
+                    for b2 in range(b + 2, nb, 2):
+                        gather(b2)
         P["ev_join"].record(side)
         main.wait_event(P["ev_join"])
 
