@@ -8,9 +8,10 @@ tokens and planned onto 8 virtual devices ("bins"):
   1. chunk_cost   realised cost of each chunk (GPU, int64)
   2. lpt_plan     longest-processing-time-first plan with equal chunk counts (GPU; the
                   same plan as the host lpt_assign, so nothing returns to the host)
-  3. per bin: context_gather of its chunks of K and V into its local buffer, then
+  3. per bin: context_gather of its chunks of K and V into its local buffer, and
      sparse_xattn_fwd (the own-block term on bin 0): partial O, lse; the bins
-     alternate between two streams, so their gathers and forwards overlap
+     alternate between two streams, each stream gathering its later bins right
+     after its first forward, so one stream's gathers overlap the other's forward
   4. lse_combine  of the 8 partials
   5. sparse_xattn_bwd: delta pre-pass, then the dQ phase of every bin (accumulated,
      on a second stream) beside the dK/dV phase of every bin (bf16 dK, dV)
