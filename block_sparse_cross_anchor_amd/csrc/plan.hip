@@ -7,10 +7,12 @@
 // the device-resident costs, so that a step needs no round trip through the host:
 //   1. rank the chunks by (cost descending, index ascending), in parallel;
 //   2. visit them in rank order: each chunk goes to the bin with the least (load,
-//      index) among those with fewer than n_chunk / n_bin chunks.  Up to kScanBins
-//      bins one thread holds them in registers (no memory access or cross-lane step on
-//      the chain from one chunk to the next); beyond, one wave's lanes hold the bins
-//      and take a wave-wide arg-min;
+//      index) among those with fewer than n_chunk / n_bin chunks.  Up to 8 bins with
+//      non-negative costs whose total stays below 2^28, eight lanes of one wave hold
+//      the bins as 32-bit keys and take the least in three DPP steps; otherwise, up to
+//      kScanBins bins, one thread holds them in registers (no memory access or
+//      cross-lane step on the chain from one chunk to the next); beyond, one wave's
+//      lanes hold the bins and take a wave-wide arg-min;
 //   3. write each bin's chunk list in increasing chunk index (the order a stable sort
 //      of the chunks by bin gives), with the chunks' global starts and lengths.
 #include "internal.h"
@@ -57,6 +59,51 @@ __device__ __forceinline__ void greedy_scan(int n, int n_bin, int cap, const lon
     if (b < n_bin) load_s[b] = ld[b];
 }
 
+// Least of the eight values held by each group of eight lanes, left in all eight:
+// swap neighbours (DPP quad_perm [1,0,3,2]), then pairs (quad_perm [2,3,0,1]), then
+// the two quads (row_half_mirror).
+__device__ __forceinline__ uint32_t min8_dpp(uint32_t m) {
+  m = min(m, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(m), 0xB1, 0xF, 0xF, false)));
+  m = min(m, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(m), 0x4E, 0xF, 0xF, false)));
+  m = min(m, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(m), 0x141, 0xF, 0xF, false)));
+  return m;
+}
+
+// The greedy visit for up to 8 bins by one full wave.  Lane b < n_bin holds bin b's
+// key (load << 3) | b, with bit 31 set once the bin holds cap chunks; every other lane
+// holds 0xffffffff.  The least key is the least (load, index) among bins with room
+// (a full bin's key exceeds every open one's while the loads stay below 2^28), so a
+// chunk costs one three-step DPP minimum, one readfirstlane and the owner's charge.
+// Each lane holds one chunk of the current block of 64 (its cost and index), so no
+// memory access sits on the chain, and lane k records the bin of the block's chunk k.
+// Valid for costs >= 0 whose total is below 2^28; n is a multiple of n_bin, so a bin
+// is always open while chunks remain.
+__device__ __forceinline__ void greedy_dpp8(int n, int n_bin, int cap, const long long* c_sorted, const int* ord,
+                                            int* bin_s, long long* load_s) {
+  const int lane = threadIdx.x % 64;
+  uint32_t key = lane < n_bin ? static_cast<uint32_t>(lane) : 0xffffffffu;
+  int ct = 0;
+  for (int k0 = 0; k0 < n; k0 += 64) {
+    const int kn = min(64, n - k0);
+    const int cl = lane < kn ? static_cast<int>(c_sorted[k0 + lane]) : 0;
+    const int ol = lane < kn ? ord[k0 + lane] : 0;
+    int mybin = 0;
+    for (int k = 0; k < kn; ++k) {
+      const uint32_t m = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(min8_dpp(key))));
+      const int bb = static_cast<int>(m & 7u);
+      const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_readlane(cl, k)) << 3;
+      if (lane == bb) {
+        key += c;
+        ct += 1;
+        if (ct == cap) key |= 0x80000000u;
+      }
+      mybin = lane == k ? bb : mybin;
+    }
+    if (lane < kn) bin_s[ol] = mybin;
+  }
+  if (lane < n_bin) load_s[lane] = static_cast<long long>((key & 0x7fffffffu) >> 3);
+}
+
 __global__ __launch_bounds__(kPlanThreads) void lpt_plan_kernel(const int64_t* __restrict__ cost, int32_t n,
                                                                 int32_t n_bin, const int32_t* __restrict__ chunk_gstart,
                                                                 const int32_t* __restrict__ chunk_len,
@@ -88,8 +135,29 @@ __global__ __launch_bounds__(kPlanThreads) void lpt_plan_kernel(const int64_t* _
     ord[rank] = i;
     c_sorted[rank] = ci;
   }
+  __shared__ long long tot_s, min_s;
+  if (tid < 64) {  // total and least cost: decides whether 32-bit keys hold the loads
+    long long t = 0, mn = 0x7fffffffffffffffLL;
+    for (int i = tid; i < n; i += 64) {
+      const long long c = c_s[i];
+      t += c < 0 ? 0 : (c < (1LL << 28) ? c : (1LL << 28));  // clamped: no overflow
+      mn = c < mn ? c : mn;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      t += __shfl_xor(t, off, 64);
+      const long long o = __shfl_xor(mn, off, 64);
+      mn = o < mn ? o : mn;
+    }
+    if (tid == 0) {
+      tot_s = t;
+      min_s = mn;
+    }
+  }
   __syncthreads();
-  if (n_bin <= kScanBins) {
+  if (n_bin <= 8 && min_s >= 0 && tot_s < (1LL << 28)) {
+    if (tid < 64) greedy_dpp8(n, n_bin, cap, c_sorted, ord, bin_s, load_s);
+  } else if (n_bin <= kScanBins) {
     if (tid == 0) {
       if (n_bin <= 8) greedy_scan<8>(n, n_bin, cap, c_sorted, ord, bin_s, load_s);
       else if (n_bin <= 16) greedy_scan<16>(n, n_bin, cap, c_sorted, ord, bin_s, load_s);

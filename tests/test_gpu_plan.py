@@ -5,6 +5,7 @@ load then index), so the device's bin of every chunk and every bin's load must e
 the oracle's exactly; each bin's chunk list must be its chunks in increasing index.
 Cases: random costs with many ties and zeros, loads far beyond 32 bits, one bin,
 one chunk per bin, bins beyond one wave (lanes owning several bins), the size limits,
+cost totals on both sides of 2^28 (up to 8 bins the greedy switches key width there),
 and the benchmark workload's GPU-priced chunks.
 """
 import numpy as np
@@ -54,6 +55,17 @@ def test_lpt_plan_edge_cases():
     rng = np.random.default_rng(7)
     _check(rng.integers(0, 1000, size=4096), 1024)           # the size limits
     _check(rng.integers(0, 10, size=4096), 8)
+    # up to 8 bins, 32-bit keys hold the loads while the cost total stays below 2^28:
+    # one case on each side of that switch, and one with a single cost past 2^63 / 4096
+    for total in (2 ** 28 - 1, 2 ** 28):
+        c = rng.integers(0, 2 ** 17, size=200 * 8).astype(np.int64)
+        c[0] += total - int(c.sum())
+        assert c.min() >= 0 and int(c.sum()) == total
+        _check(c, 8)
+        _check(c, 5)
+    c = rng.integers(0, 3, size=64).astype(np.int64)
+    c[5] = 2 ** 62
+    _check(c, 8)
 
 
 @pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
