@@ -399,6 +399,8 @@ struct DkdvSched {
   const int32_t* share_tile;  // [n_shares]: tile holding each share's first list unit
   int32_t* hits;           // [n_tiles][hit_stride]: the hit steps of each tile, in order
                            // (nullptr when the lists would exceed kMaxListEntries: then scanned)
+  int4* hits_iv;           // [n_tiles][hit_stride]: beside each listed step, the key intervals
+                           // of its two blocks (as the step loop reads them from step_iv)
   int64_t hit_stride;      // query steps of a kv head (the most hits a tile can have)
   float* slots;            // [2 n_shares][kKeysPerWG][2][D]: partial dK, dV
 };
@@ -485,6 +487,7 @@ __global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched 
   // hit steps in increasing order: batch by batch, each hit at (hits before the batch)
   // + (hits of lower waves) + (hits of lower lanes)
   int32_t* list = sc.hits != nullptr ? sc.hits + static_cast<int64_t>(t) * sc.hit_stride : nullptr;
+  int4* list_iv = sc.hits != nullptr ? sc.hits_iv + static_cast<int64_t>(t) * sc.hit_stride : nullptr;
   int n = 0, first = sg.n_steps;
   for (int base = 0; base < sg.n_steps; base += 256) {
     const bool hit = step_hit(p, sg, base + tid, n_q, self_tile, kmin, kmax);
@@ -500,7 +503,14 @@ __global__ __launch_bounds__(256) void dkdv_count_kernel(BwdParams p, DkdvSched 
     }
     if (hit) {
       const int pos = n + pre + __popcll(m & ((uint64_t{1} << (tid % 64)) - 1));
-      if (list != nullptr) list[pos] = base + tid;
+      if (list != nullptr) {
+        const int st = base + tid;
+        const int tk = sg.tok0(st);
+        const int b0 = tk / kBlock, b1 = (tk + sg.ntok(st, n_q) - 1) / kBlock;
+        list[pos] = st;
+        list_iv[pos] = self_tile ? int4{kBlock * b0, kBlock * b0 + kBlock, kBlock * b1, kBlock * b1 + kBlock}
+                                 : int4{p.sample_start[b0], p.anchor[b0], p.sample_start[b1], p.anchor[b1]};
+      }
       if (pos == 0) red[1][0] = base + tid;  // the first hit (read after the loop)
     }
     n += cnt;
@@ -620,11 +630,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
       const int ue = static_cast<int>(min<int64_t>(u1, r + (end - pos)));  // end of this share in the tile
       pos += ue - r;
       if (max(r, u0) >= ue) continue;  // only the tile's setup units fall in this share
-      const int4 ti = sc.tinfo[t];
-      kmin = __builtin_amdgcn_readfirstlane(ti.x);
-      kmax = __builtin_amdgcn_readfirstlane(ti.y);
-      hits = __builtin_amdgcn_readfirstlane(ti.z);
-      scan0 = __builtin_amdgcn_readfirstlane(ti.w);
+      const int32_t* ti = reinterpret_cast<const int32_t*>(sc.tinfo) + 4 * static_cast<int64_t>(t);
+      kmin = ld_uniform(ti, 0);  // scalar loads: no wait for this wave's stores in flight
+      kmax = ld_uniform(ti, 1);
+      hits = ld_uniform(ti, 2);
+      scan0 = ld_uniform(ti, 3);
       s0 = max(r, u0) - u0;
       s1 = ue - u0;
     } else {
@@ -637,6 +647,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
     const bool self_tile = t >= sc.n_ctx_tiles;
     const int64_t key_rows = self_tile ? n_q : p.n_loc;
     const int64_t krow0 = static_cast<int64_t>(self_tile ? t - sc.n_ctx_tiles : t) * kKeysPerWG;
+    // Per-lane constants are derived anew in every segment from an opaque copy of the
+    // lane index: held across segments they were spilled, and their reloads waited for
+    // the previous segment's stores.
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, wave = __builtin_amdgcn_readfirstlane(tid_o / 64), lane = tid_o % 64;
+    const int h2 = lane / 32, l32 = lane % 32;
 
     // this lane's keys (columns of the two S tiles): local rows and key coordinates
     int krow[H], kcoord[H];
@@ -652,16 +669,38 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
     // vtile, the list and the stages; this one only orders `red` (tile mode) and lets
     // the previous write-back stay in flight while this segment's copies start.
     lds_barrier();
-    {  // V rows of the tile -> LDS (direct copies into the swizzled layout)
-      const uint16_t* V = self_tile ? p.v_self : p.v;
+    // Stream-K: the segment's first batch of hit steps [s0, s0 + cnt0) and their key
+    // intervals, copied from the count pass's lists straight into LDS (lanes past the
+    // batch repeat its last entry into unused places); later batches, if any, are
+    // collected by the scan below.  With the tile's copies and the K loads that follow,
+    // the segment's loads are in flight together and one wait covers them.
+    int cnt0 = 0;
+    if (streamk && sc.hits != nullptr) {
+      cnt0 = min(kListCap, s1 - s0);
+      const int64_t l0 = static_cast<int64_t>(t) * sc.hit_stride + s0;
+#pragma unroll
+      for (int k = 0; k < kListCap / kT; ++k) {
+        const int i0 = k * kT + wave * 64;  // the wave's first entry (wave-uniform)
+        if (i0 < cnt0) {
+          const uint32_t i = static_cast<uint32_t>(min(i0 + lane, cnt0 - 1));
+          dma4_s(sc.hits + l0, 4 * i, lds_addr(&step_list[i0]));
+          dma16_s(sc.hits_iv + l0, 16 * i, lds_addr(&step_iv[i0]));
+        }
+      }
+    }
+    {  // V rows of the tile -> LDS (direct copies into the swizzled layout; rows past
+       // the key rows repeat the last one)
+      const uint16_t* V = (self_tile ? p.v_self : p.v) + (krow0 * p.hkv + g) * D;
+      const int last = static_cast<int>(min<int64_t>(kKeysPerWG, key_rows - krow0)) - 1;
       constexpr int VI = kKeysPerWG * CPR / kT;  // copies per lane
 #pragma unroll
       for (int j = 0; j < VI; ++j) {
         const int inst = wave * VI + j;
         const int c = inst * 64 + lane, row = c / CPR;
         const int logical = (c % CPR) ^ LdsTile<D>::swz(row);
-        const int64_t src_row = min(krow0 + row, key_rows - 1);
-        dma16(V + (src_row * p.hkv + g) * D + 8 * logical, lds_addr(vtile + inst * 512));
+        const uint32_t off = 2u * (static_cast<uint32_t>(min(row, last)) * static_cast<uint32_t>(p.hkv * D) +
+                                   8u * static_cast<uint32_t>(logical));
+        dma16_s(V, off, lds_addr(vtile + inst * 512));
       }
     }
 #pragma unroll
@@ -704,26 +743,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
         for (int ks = 0; ks < KS; ++ks)
           kf[hh][ks] = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(K + (krc[hh] * p.hkv + g) * D + 16 * ks + 8 * h2));
-    }
-    // Stream-K: the segment's first batch of hit steps [s0, s0 + cnt0) from the count
-    // pass's list, loaded beside the tile loads (before the accumulators are live);
-    // later batches, if any, are collected by the scan below.
-    int cnt0 = 0;
-    if (streamk && sc.hits != nullptr) {
-      cnt0 = min(kListCap, s1 - s0);
-      const int32_t* list = sc.hits + static_cast<int64_t>(t) * sc.hit_stride + s0;
-#pragma unroll
-      for (int k = 0; k < kListCap / kT; ++k) {
-        const int i = k * kT + tid;
-        if (i < cnt0) {
-          const int st = list[i];
-          const int tk = sg.tok0(st);
-          const int b0 = tk / kBlock, b1 = (tk + sg.ntok(st, n_q) - 1) / kBlock;
-          step_list[i] = st;
-          step_iv[i] = self_tile ? int4{kBlock * b0, kBlock * b0 + kBlock, kBlock * b1, kBlock * b1 + kBlock}
-                                 : int4{p.sample_start[b0], p.anchor[b0], p.sample_start[b1], p.anchor[b1]};
-        }
-      }
     }
     wait_vmcnt<0>();  // the segment's own loads are complete before the copy pipeline starts
     f32x16 dkacc[H][DT], dvacc[H][DT];
@@ -1041,12 +1060,13 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(BwdParams p, DkdvSched
   }
 }
 
-// Hit lists are kept up to this many (tile, step) entries (256 MiB); larger calls scan.
-constexpr int64_t kMaxListEntries = int64_t{1} << 26;
+// Hit lists (a step index and its blocks' key intervals, 20 bytes per entry) are kept
+// up to this many (tile, step) entries (320 MiB); larger calls scan.
+constexpr int64_t kMaxListEntries = int64_t{1} << 24;
 
 struct WsLayout {
-  int64_t n_tiles, n_shares, hit_stride, prefix_off, tinfo_off, coord_off, share_off, hits_off, order_off, slots_off,
-      bytes;
+  int64_t n_tiles, n_shares, hit_stride, prefix_off, tinfo_off, coord_off, share_off, hits_off, hits_iv_off,
+      order_off, slots_off, bytes;
   bool lists;
 };
 
@@ -1067,7 +1087,8 @@ WsLayout ws_layout(int64_t n_blk, int64_t n_loc, int64_t d, int64_t grp) {
   L.share_off = L.coord_off + up(4 * n_loc);
   L.hits_off = L.share_off + up(4 * L.n_shares);
   L.lists = L.n_tiles * L.hit_stride <= kMaxListEntries;
-  L.order_off = L.hits_off + (L.lists ? up(4 * L.n_tiles * L.hit_stride) : 0);
+  L.hits_iv_off = L.hits_off + (L.lists ? up(4 * L.n_tiles * L.hit_stride) : 0);
+  L.order_off = L.hits_iv_off + (L.lists ? up(16 * L.n_tiles * L.hit_stride) : 0);
   L.slots_off = L.order_off + up(4 * (groups < kMaxOrderedGroups ? groups : int64_t{kMaxOrderedGroups}));
   L.bytes = L.slots_off + 2 * L.n_shares * static_cast<int64_t>(kKeysPerWG) * 2 * d * 4;
   return L;
@@ -1151,6 +1172,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   sc.coord = nullptr;
   sc.share_tile = nullptr;
   sc.hits = nullptr;
+  sc.hits_iv = nullptr;
   sc.hit_stride = 0;
   sc.slots = nullptr;
   if (a.workspace != nullptr) {
@@ -1166,6 +1188,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
     int32_t* share_tile = reinterpret_cast<int32_t*>(ws + L.share_off);
     sc.share_tile = share_tile;
     sc.hits = L.lists ? reinterpret_cast<int32_t*>(ws + L.hits_off) : nullptr;
+    sc.hits_iv = L.lists ? reinterpret_cast<int4*>(ws + L.hits_iv_off) : nullptr;
     sc.hit_stride = L.hit_stride;
     sc.slots = reinterpret_cast<float*>(ws + L.slots_off);
     dkdv_count_kernel<<<dim3(static_cast<unsigned>(n_tiles)), dim3(256), 0, s>>>(p, sc, prefix, tinfo, coord);

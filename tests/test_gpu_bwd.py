@@ -393,14 +393,14 @@ def test_dkdv_stream_k_segments_longer_than_one_step_batch(hq, n_blk):
 
 
 def test_dkdv_stream_k_without_hit_lists():
-    """Calls whose (tile, query step) lists would exceed 2^26 entries keep no lists:
-    every stream-K segment then collects its steps by scanning.  A 1M-token context of
-    2048-token samples, 8192 queries, head group 40 (16384 query steps): the
+    """Calls whose (tile, query step) lists would exceed 2^24 entries keep no lists:
+    every stream-K segment then collects its steps by scanning.  A 256k-token context
+    of 2048-token samples, 8192 queries, head group 40 (16384 query steps): the
     load-balanced dK/dV phase must give the one-workgroup-per-tile phase's sums."""
-    hq, hkv, d, n_ctx, n_blk = 40, 1, 64, 1 << 20, 512
+    hq, hkv, d, n_ctx, n_blk = 40, 1, 64, 1 << 18, 512
     n_tiles = n_ctx // 256 + 16 * n_blk // 256
     n_steps = 16 * n_blk * 2              # one token per step, two steps per token
-    assert n_tiles * n_steps > 1 << 26
+    assert n_tiles * n_steps > 1 << 24
     meta = synth.draw_meta(77, n_ctx, 2048, 2048, n_blk)
     gs, gl = synth.contiguous_chunks(n_ctx, 1024)
     inp = synth.draw_inputs(77, meta, hq, hkv, d, "bf16", 1.0 / math.sqrt(d), gs, gl, with_dout=True)
