@@ -386,9 +386,12 @@ static_assert(kListCap % (64 * kKvWaves) == 0, "a list batch splits evenly over 
 // Stream-K list units: a tile with hits occupies kSetupUnits + hits consecutive units
 // of the per-head list (the first ones stand for its setup, step list and write-back,
 // so that a share that starts many short tiles gets fewer steps); a tile without
-// hits, none.  Measured, a segment's fixed work takes about as long as 7 to 9 steps,
-// and the kernel time is flat for weights 9 to 13.
-constexpr int kSetupUnits = 10;
+// hits, none.  Measured, a segment's fixed work takes about as long as 7 to 8 steps;
+// weights 6, 7 and 8 were slower than 10 (more tiles cut), and 9 to 13 time the same.
+#ifndef SXA_KV_SETUP_UNITS
+#define SXA_KV_SETUP_UNITS 10
+#endif
+constexpr int kSetupUnits = SXA_KV_SETUP_UNITS;
 
 struct DkdvSched {
   int32_t n_ctx_tiles, n_tiles;
@@ -575,11 +578,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
   constexpr int NI = 2 * kStepRows * CPR / kT;  // 16-byte copies per lane and step (Q, dO)
   static_assert(NI >= 1 && NI * kT == 2 * kStepRows * CPR, "stage copy must split evenly over lanes");
   constexpr int SE = 2 * kStepRows * D;  // elements of one stage: Q rows, then dO rows
+  constexpr int kVCopies = kKeysPerWG * CPR / kT;  // 16-byte V tile copies per lane
   __shared__ __attribute__((aligned(256))) uint16_t vtile[kKeysPerWG * D];
   __shared__ __attribute__((aligned(256))) uint16_t stg[kStageBufs][SE];
   __shared__ __attribute__((aligned(16))) float smeta[kStageBufs][2 * kStepRows];  // lse2 rows, delta rows
   __shared__ int step_list[kListCap];
   __shared__ int4 step_iv[kListCap];  // key intervals of the listed step's two blocks
+  __shared__ int kco[kKeysPerWG];     // stream-K context tiles: key coordinate of each row
   __shared__ int wave_cnt[kWaves];
   __shared__ int red[2][kWaves];
 
@@ -669,11 +674,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
     // vtile, the list and the stages; this one only orders `red` (tile mode) and lets
     // the previous write-back stay in flight while this segment's copies start.
     lds_barrier();
+    // Key coordinates: stream-K context tiles copy the count pass's coordinates of the
+    // tile's rows into LDS (each lane reads its own after the pipeline's first
+    // barrier, so no register waits on a load across segments); own-block tiles use
+    // the row itself; without a workspace they are computed here.
+    const bool kco_lds = streamk && !self_tile;
+    const int last_row = static_cast<int>(min<int64_t>(kKeysPerWG, key_rows - krow0)) - 1;
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh)
+      kcoord[hh] = self_tile ? static_cast<int>(krc[hh]) : (streamk ? 0 : key_coord(p, false, krc[hh]));
+    if (kco_lds && wave < kKeysPerWG / 64)
+      dma4_s(sc.coord + krow0, 4u * static_cast<uint32_t>(min(wave * 64 + lane, last_row)), lds_addr(&kco[wave * 64]));
     // Stream-K: the segment's first batch of hit steps [s0, s0 + cnt0) and their key
     // intervals, copied from the count pass's lists straight into LDS (lanes past the
     // batch repeat its last entry into unused places); later batches, if any, are
-    // collected by the scan below.  With the tile's copies and the K loads that follow,
-    // the segment's loads are in flight together and one wait covers them.
+    // collected by the scan below.  The tile's copies and the K loads follow, and the
+    // segment waits only for the lists before it issues its first step copies: the
+    // tile's loads stay in flight until the pipeline's first wait.
     int cnt0 = 0;
     if (streamk && sc.hits != nullptr) {
       cnt0 = min(kListCap, s1 - s0);
@@ -691,21 +708,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
     {  // V rows of the tile -> LDS (direct copies into the swizzled layout; rows past
        // the key rows repeat the last one)
       const uint16_t* V = (self_tile ? p.v_self : p.v) + (krow0 * p.hkv + g) * D;
-      const int last = static_cast<int>(min<int64_t>(kKeysPerWG, key_rows - krow0)) - 1;
-      constexpr int VI = kKeysPerWG * CPR / kT;  // copies per lane
 #pragma unroll
-      for (int j = 0; j < VI; ++j) {
-        const int inst = wave * VI + j;
+      for (int j = 0; j < kVCopies; ++j) {
+        const int inst = wave * kVCopies + j;
         const int c = inst * 64 + lane, row = c / CPR;
         const int logical = (c % CPR) ^ LdsTile<D>::swz(row);
-        const uint32_t off = 2u * (static_cast<uint32_t>(min(row, last)) * static_cast<uint32_t>(p.hkv * D) +
+        const uint32_t off = 2u * (static_cast<uint32_t>(min(row, last_row)) * static_cast<uint32_t>(p.hkv * D) +
                                    8u * static_cast<uint32_t>(logical));
         dma16_s(V, off, lds_addr(vtile + inst * 512));
       }
     }
-#pragma unroll
-    for (int hh = 0; hh < H; ++hh)
-      kcoord[hh] = self_tile ? static_cast<int>(krc[hh]) : (streamk ? sc.coord[krc[hh]] : key_coord(p, false, krc[hh]));
     if (!streamk) {
       kmin = 0x7fffffff;
       kmax = -0x7fffffff;
@@ -744,7 +756,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
           kf[hh][ks] = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(K + (krc[hh] * p.hkv + g) * D + 16 * ks + 8 * h2));
     }
-    wait_vmcnt<0>();  // the segment's own loads are complete before the copy pipeline starts
+    // The list copies are done once at most the kVCopies + H KS loads issued after them
+    // are in flight (vector loads complete in issue order); the compiler barrier keeps
+    // those K loads above the wait.
+    asm volatile("" ::: "memory");
+    wait_vmcnt<kVCopies + H * KS>();
     f32x16 dkacc[H][DT], dvacc[H][DT];
 #pragma unroll
     for (int hh = 0; hh < H; ++hh)
@@ -817,14 +833,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
       }
 
       // ---- pipeline over the listed steps in groups of kStepsPerSync: iteration j
-      // waits for group j, copies group j + 1 into the stages group j - 1 used, then
-      // computes group j.  Nothing else may be in flight while the copies are counted.
-      wait_vmcnt<0>();
+      // waits for group j (every load of this wave, the tile's included), copies group
+      // j + 1 into the stages group j - 1 used, then computes group j.
       const int ngrp = (cnt + kStepsPerSync - 1) / kStepsPerSync;
       for (int jg = -1; jg < ngrp; ++jg) {
         if (jg >= 0) {
           wait_vmcnt<0>();    // this wave's copies of group jg landed
           barrier_nofence();  // every wave's; group jg - 1's stages are no longer read
+          if (jg == 0 && kco_lds) {  // the tile's copies (coordinates included) have landed
+#pragma unroll
+            for (int hh = 0; hh < H; ++hh) kcoord[hh] = kco[krow[hh]];
+          }
         }
 #pragma unroll
         for (int q = 0; q < kStepsPerSync; ++q) {
