@@ -950,24 +950,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
               sacc[hh][r] = ok ? sacc[hh][r] : -INFINITY;
             }
         }
-        // P = exp2(.) and dS = P (dP - delta) as bf16 pairs
+        // P = exp2(.) and dS = P (dP - delta) as bf16 pairs.  Accumulator rows 8 j +
+        // rel + (0..3) of j = 0, 1 feed the dV, dK products' first k-half (kq = 0), those
+        // of j = 2, 3 the second; the second half's exponents and products are formed
+        // between the first half's MFMAs (four quarters of two rows over its DT k-steps).
         u32x4 pw[H][2], sw[H][2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&smeta[sb][kStepRows + 8 * j + 4 * h2]);
+        auto p_ds = [&](int j, int half, const f32x4& d4) {
 #pragma unroll
           for (int hh = 0; hh < H; ++hh) {
-            float pr[4], ds[4];
-#pragma unroll
-            for (int i2 = 0; i2 < 4; ++i2) {
-              pr[i2] = __builtin_amdgcn_exp2f(sacc[hh][4 * j + i2]);
-              ds[i2] = pr[i2] * (pacc[hh][4 * j + i2] - d4[i2]);
-            }
-            pw[hh][j / 2][2 * (j % 2)] = pack_bf16x2(pr[0], pr[1]);
-            pw[hh][j / 2][2 * (j % 2) + 1] = pack_bf16x2(pr[2], pr[3]);
-            sw[hh][j / 2][2 * (j % 2)] = pack_bf16x2(ds[0], ds[1]);
-            sw[hh][j / 2][2 * (j % 2) + 1] = pack_bf16x2(ds[2], ds[3]);
+            const int r = 4 * j + 2 * half;
+            const float p0 = __builtin_amdgcn_exp2f(sacc[hh][r]), p1 = __builtin_amdgcn_exp2f(sacc[hh][r + 1]);
+            const float s0 = p0 * (pacc[hh][r] - d4[2 * half]), s1 = p1 * (pacc[hh][r + 1] - d4[2 * half + 1]);
+            pw[hh][j / 2][2 * (j % 2) + half] = pack_bf16x2(p0, p1);
+            sw[hh][j / 2][2 * (j % 2) + half] = pack_bf16x2(s0, s1);
           }
+        };
+        f32x4 d4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d4[j] = *reinterpret_cast<const f32x4*>(&smeta[sb][kStepRows + 8 * j + 4 * h2]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          p_ds(j, 0, d4[j]);
+          p_ds(j, 1, d4[j]);
         }
         bf16x8 dta = lds_frag_t(ta + kDoOff, tb + kDoOff), qta = lds_frag_t(ta, tb);
 #pragma unroll
@@ -987,6 +991,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * kKvWaves, 64 * kKvWav
             dkacc[hh][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cqt, __builtin_bit_cast(bf16x8, sw[hh][kq]),
                                                                     dkacc[hh][dt], 0, 0, 0);
           }
+          // the second k-half's four quarters, spread over the first half's DT k-steps
+#pragma unroll
+          for (int qq = 4 * kd / DT; qq < 4 * (kd + 1) / DT && kd < DT; ++qq) p_ds(2 + qq / 2, qq % 2, d4[2 + qq / 2]);
           __builtin_amdgcn_sched_barrier(0);
         }
         }  // steps of the group
